@@ -1,0 +1,189 @@
+"""CPU oracle for the MoE dispatch/combine path (test infrastructure).
+
+Only the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
+leg may import this package. The HIP library and its binding never do.
+
+The arithmetic lives in ``moe_oracle.c`` (plain single-threaded C, fp64 where
+the method leaves the precision open). This module builds it with gcc and
+wraps its functions for numpy arrays. bf16 arrays are uint16 bit patterns,
+E4M3 arrays are uint8 codes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import NamedTuple, Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB = os.path.join(_HERE, "libmoeoracle.so")
+
+GCC_CMD = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+           "-fno-fast-math", "-Wall", "-Wextra", "-o", _LIB, _SRC, "-lm"]
+
+
+def build() -> str:
+    """Compile the oracle with gcc; returns the library path."""
+    subprocess.run(GCC_CMD, check=True)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    i64, i32 = ctypes.c_int64, ctypes.c_int
+    lib.oracle_route_topk.argtypes = [P, i64, i32, i32, P, P]
+    lib.oracle_route_topk.restype = None
+    lib.oracle_dispatch.argtypes = [P, P, i64, i32, i32, i32, i32, i32, i32,
+                                    P, P, P, P, P, P, P]
+    lib.oracle_dispatch.restype = i64
+    lib.oracle_expert_scale.argtypes = [P, P, P, P, i64, i32, i32, i32, i32, P]
+    lib.oracle_expert_scale.restype = None
+    lib.oracle_combine.argtypes = [P, P, P, i64, i32, i32, P]
+    lib.oracle_combine.restype = None
+    lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+    lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+    lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_value.restype = ctypes.c_float
+    lib.oracle_bf16_from_double.argtypes = [ctypes.c_double]
+    lib.oracle_bf16_from_double.restype = ctypes.c_uint16
+    lib.oracle_quantize_block.argtypes = [P, P, P]
+    lib.oracle_quantize_block.restype = None
+    lib.oracle_e4m3_encode_array.argtypes = [P, P, i64]
+    lib.oracle_e4m3_encode_array.restype = None
+    lib.oracle_e4m3_encode_bits.argtypes = [ctypes.c_uint32, i64, P]
+    lib.oracle_e4m3_encode_bits.restype = None
+    _lib = lib
+    return lib
+
+
+def _p(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def route_topk(logits: np.ndarray, k: int):
+    """(topk_idx int32 [T,k], topk_w float32 [T,k])."""
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    idx = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float32)
+    _load().oracle_route_topk(_p(logits), T, E, k, _p(idx), _p(w))
+    return idx, w
+
+
+class Dispatch(NamedTuple):
+    out: np.ndarray            # [num_rows, H] uint16 (bf16) or uint8 (E4M3)
+    scales: Optional[np.ndarray]  # [num_rows, H/128] float32, FP8 only
+    expert_counts: np.ndarray  # [E]
+    expert_offsets: np.ndarray  # [E+1]
+    group_offsets: np.ndarray  # [G+1]
+    row_src: np.ndarray        # [num_rows]
+    dst_row: np.ndarray        # [T,k]
+    num_rows: int
+
+
+def max_rows(T: int, E: int, k: int, row_align: int) -> int:
+    return T * k + E * (row_align - 1)
+
+
+def dispatch(x: np.ndarray, topk_idx: np.ndarray, E: int, groups: int = 1,
+             row_align: int = 1, fp8: bool = False) -> Dispatch:
+    x = _c(x, np.uint16)
+    topk_idx = _c(topk_idx, np.int32)
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    cap = max_rows(T, E, k, row_align)
+    out = np.zeros((cap, H), np.uint8 if fp8 else np.uint16)
+    scales = np.zeros((cap, H // 128), np.float32) if fp8 else None
+    counts = np.empty(E, np.int32)
+    offs = np.empty(E + 1, np.int32)
+    goff = np.empty(groups + 1, np.int32)
+    row_src = np.full(cap, -2, np.int32)
+    dst_row = np.empty((T, k), np.int32)
+    R = _load().oracle_dispatch(_p(x), _p(topk_idx), T, H, E, k, groups, row_align,
+                                int(fp8), _p(out), _p(scales), _p(counts), _p(offs),
+                                _p(goff), _p(row_src), _p(dst_row))
+    R = int(R)
+    return Dispatch(out[:R], None if scales is None else scales[:R], counts, offs,
+                    goff, row_src[:R], dst_row, R)
+
+
+def expert_scale(d: Dispatch, topk_idx: np.ndarray, E: int, fp8: bool,
+                 identity: bool = False) -> np.ndarray:
+    """Stand-in experts: bf16 [num_rows, H]."""
+    H = d.out.shape[1]
+    topk_idx = _c(topk_idx, np.int32)
+    y = np.empty((d.num_rows, H), np.uint16)
+    disp = _c(d.out, np.uint8 if fp8 else np.uint16)
+    sc = _c(d.scales, np.float32) if fp8 else None
+    _load().oracle_expert_scale(_p(disp), _p(sc), _p(_c(d.row_src, np.int32)),
+                                _p(topk_idx), d.num_rows, H, E, int(fp8),
+                                int(identity), _p(y))
+    return y
+
+
+def combine(expert_out: np.ndarray, dst_row: np.ndarray, topk_w: np.ndarray) -> np.ndarray:
+    """y bf16 [T,H] (uint16)."""
+    expert_out = _c(expert_out, np.uint16)
+    dst_row = _c(dst_row, np.int32)
+    topk_w = _c(topk_w, np.float32)
+    T, k = dst_row.shape
+    H = expert_out.shape[1]
+    y = np.empty((T, H), np.uint16)
+    _load().oracle_combine(_p(expert_out), _p(dst_row), _p(topk_w), T, H, k, _p(y))
+    return y
+
+
+def e4m3_encode(v: float) -> int:
+    return int(_load().oracle_e4m3_encode(float(v)))
+
+
+def e4m3_value(code: int) -> float:
+    return float(_load().oracle_e4m3_value(int(code)))
+
+
+def e4m3_encode_array(v: np.ndarray) -> np.ndarray:
+    """Elementwise E4M3 codes of a float32 array."""
+    v = _c(v, np.float32)
+    out = np.empty(v.shape, np.uint8)
+    _load().oracle_e4m3_encode_array(_p(v), _p(out), v.size)
+    return out
+
+
+def e4m3_encode_bits(start: int, count: int) -> np.ndarray:
+    """E4M3 codes of the float32 bit patterns start .. start+count-1."""
+    out = np.empty(count, np.uint8)
+    _load().oracle_e4m3_encode_bits(start, count, _p(out))
+    return out
+
+
+def bf16_from_double(d: float) -> int:
+    return int(_load().oracle_bf16_from_double(float(d)))
+
+
+def quantize_block(xblock: np.ndarray):
+    """(codes uint8 [128], scale float32) for one 128-element bf16 block."""
+    xb = _c(xblock, np.uint16)
+    assert xb.shape == (128,)
+    q = np.empty(128, np.uint8)
+    s = np.empty(1, np.float32)
+    _load().oracle_quantize_block(_p(xb), _p(q), _p(s))
+    return q, s[0]

@@ -1,0 +1,319 @@
+/*
+ * CPU oracle for the MoE token dispatch / combine path.
+ *
+ * TEST INFRASTRUCTURE ONLY. Plain, slow, single-threaded C that states what
+ * the path computes. Only the tests, the smoke check and the benchmark's CPU
+ * baseline use it; the HIP library never links, includes or calls it, and
+ * the two share no source. Build: gcc -O2 -std=c11 -fPIC -shared (no
+ * fast-math, SSE arithmetic, default round-to-nearest-even mode).
+ *
+ * Sources (Perplexity engineering posts):
+ *  [EPMC] "Efficient and portable mixture-of-experts communication",
+ *         sections Introduction, Dispatch, Combine.
+ *  [EFA]  "Enabling trillion-parameter models on AWS EFA",
+ *         sections Send and receive buffers, Dispatch and Combine,
+ *         Evaluation (dispatch/combine latency).
+ *  [DSV3] DeepSeek-V3 report excerpts quoted on the third and fourth pages
+ *         (fine-grained 1x128 activation quantisation; gating kept in its
+ *         original precision; combine components kept in BF16).
+ *
+ * Readings where the pages are silent (each is repeated where it is used):
+ *  - selection is on the raw fp32 logits, descending, ties to the lower
+ *    expert index, IEEE comparison (so -0 == +0);
+ *  - weights are the router softmax restricted to the selected experts and
+ *    renormalised to sum to one, computed in fp64 and rounded once to fp32;
+ *  - within an expert segment rows are in token order (a stable layout);
+ *  - segments are padded to a multiple of row_align rows; pad rows carry a
+ *    zero payload, zero scales and row_src = -1;
+ *  - destination groups are contiguous expert ranges of E/G experts;
+ *  - FP8 is OCP E4M3 (bias 7, max 448, no infinities); the scale of a
+ *    1x128 block is s = amax / 448 (fp32 division); each element is the fp32
+ *    quotient x / s rounded to nearest-even E4M3 and saturated to +-448;
+ *    an all-zero block has s = 0 and all codes 0x00;
+ *  - a slot whose expert id lies outside [0, E) is dropped: it is not
+ *    counted, gets dst_row = -1 and contributes nothing to combine;
+ *  - combine accumulates in fp64 in slot order and rounds once to bf16.
+ *
+ * Parity status: every function below is pinned by the CPU tests (brute
+ * force, library routines, closed forms, invariants). The composition of
+ * the whole chain has no printed values on the pages to pin against.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#include <stdlib.h>
+
+/* ---------------------------------------------------------------- bf16 */
+
+static float bf16_value(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* Round a finite double to the nearest bfloat16, ties to even, in one step
+ * (no intermediate rounding to float). bf16 keeps 8 significant bits and the
+ * float exponent range; below 2^-126 the spacing is the subnormal 2^-133. */
+uint16_t oracle_bf16_from_double(double d) {
+    uint16_t sign = signbit(d) ? 0x8000u : 0u;
+    double a = fabs(d);
+    if (a == 0.0) return sign;
+    int ex;
+    frexp(a, &ex);                 /* a = m * 2^ex, m in [0.5, 1) */
+    int q = ex - 8;                /* spacing of 8-bit significands: 2^(ex-8) */
+    if (q < -133) q = -133;        /* subnormal bf16 spacing */
+    double n = nearbyint(ldexp(a, -q));   /* exact scaling, then RNE */
+    double v = ldexp(n, q);
+    if (v >= 0x1p128) return (uint16_t)(sign | 0x7F80u);   /* overflow: inf */
+    float f = (float)v;            /* exact: v has at most 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(sign | (u >> 16));
+}
+
+/* ---------------------------------------------------------------- e4m3 */
+
+/* OCP E4M3 (FN variant) value of a code; 0x7F / 0xFF are NaN. */
+float oracle_e4m3_value(uint8_t c) {
+    int s = c >> 7, e = (c >> 3) & 0xF, m = c & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) v = ldexp((double)m, -9);            /* subnormal: m/8 * 2^-6 */
+    else v = ldexp(8.0 + m, e - 7 - 3);              /* (1 + m/8) * 2^(e-7) */
+    return (float)(s ? -v : v);
+}
+
+/* Round a finite float to nearest-even E4M3, saturating to +-448 (0x7E).
+ * Spacing: 2^-9 below 2^-6 (subnormals), else 2^(e-3) for a in [2^e, 2^(e+1)).
+ * The rounded significand n (0..16) is added to the exponent field so a
+ * carry from n == 16 moves to the next binade by itself. */
+uint8_t oracle_e4m3_encode(float v) {
+    uint8_t sign = signbit(v) ? 0x80u : 0u;
+    double a = fabs((double)v);
+    if (isnan(v)) return (uint8_t)(sign | 0x7Fu);
+    if (a > 448.0) return (uint8_t)(sign | 0x7Eu);    /* saturate to +-448 */
+    if (a < 0x1p-6) {
+        int n = (int)nearbyint(ldexp(a, 9));          /* 0..8; 8 = 2^-6 = 0x08 */
+        return (uint8_t)(sign | n);
+    }
+    int ex;
+    frexp(a, &ex);
+    int e = ex - 1;                                   /* a in [2^e, 2^(e+1)) */
+    int n = (int)nearbyint(ldexp(a, 3 - e));          /* 8..16 */
+    int code = ((e + 7) << 3) + (n - 8);             /* <= 0x7E since a <= 448 */
+    return (uint8_t)(sign | code);
+}
+
+/* Quantise one 1x128 block: s = amax/448 (fp32), q = E4M3(fp32(x/s)). */
+void oracle_quantize_block(const uint16_t* x, uint8_t* q, float* s_out) {
+    float amax = 0.0f;
+    for (int i = 0; i < 128; i++) {
+        float a = fabsf(bf16_value(x[i]));
+        if (a > amax) amax = a;
+    }
+    float s = amax / 448.0f;
+    *s_out = s;
+    for (int i = 0; i < 128; i++) {
+        if (amax == 0.0f) { q[i] = 0; continue; }
+        float y = bf16_value(x[i]) / s;               /* correctly rounded fp32 */
+        q[i] = oracle_e4m3_encode(y);
+    }
+}
+
+/* ---------------------------------------------------------------- routing */
+
+/* Router gate: softmax over the E logits of each token, the top-k experts by
+ * score, and weights renormalised over the selected experts ([EPMC]
+ * Introduction; gating in original precision per [DSV3]). Softmax is strictly
+ * increasing in the logit, so ranking by logit is ranking by probability;
+ * ranking on the fp32 logits avoids ties that rounding of probabilities would
+ * create. Slot j holds the j-th best expert. */
+void oracle_route_topk(const float* logits, int64_t T, int E, int k,
+                       int32_t* topk_idx, float* topk_w) {
+    double* p = (double*)malloc(sizeof(double) * (size_t)E);
+    unsigned char* taken = (unsigned char*)malloc((size_t)E);
+    for (int64_t t = 0; t < T; t++) {
+        const float* l = logits + t * (int64_t)E;
+        /* softmax over all experts, in fp64 */
+        double lmax = l[0];
+        for (int e = 1; e < E; e++) if (l[e] > lmax) lmax = l[e];
+        double z = 0.0;
+        for (int e = 0; e < E; e++) { p[e] = exp((double)l[e] - lmax); z += p[e]; }
+        for (int e = 0; e < E; e++) p[e] /= z;
+        /* top-k: repeatedly take the best remaining expert */
+        memset(taken, 0, (size_t)E);
+        for (int j = 0; j < k; j++) {
+            int best = -1;
+            for (int e = 0; e < E; e++) {
+                if (taken[e]) continue;
+                if (best < 0 || l[e] > l[best]) best = e;   /* ties keep lower e */
+            }
+            taken[best] = 1;
+            topk_idx[t * k + j] = best;
+        }
+        /* renormalise the selected probabilities */
+        double sel = 0.0;
+        for (int j = 0; j < k; j++) sel += p[topk_idx[t * k + j]];
+        for (int j = 0; j < k; j++)
+            topk_w[t * k + j] = (float)(p[topk_idx[t * k + j]] / sel);
+    }
+    free(p);
+    free(taken);
+}
+
+/* ---------------------------------------------------------------- dispatch */
+
+/* Count tokens per expert, turn the (padded) counts into segment offsets by a
+ * running sum, then place every (token, slot) pair into its expert's
+ * contiguous segment ([EFA] Dispatch and Combine: per-expert counts, their
+ * cumulative sum gives the offsets used to pack tokens into contiguous
+ * per-expert send buffers; [EPMC] Dispatch: payload, scales and the token's
+ * index are packed together, source and token index kept per row).
+ *
+ * Layout produced:
+ *   expert_counts[e]   tokens routed to e (unpadded)
+ *   expert_offsets[e]  first row of e's segment; expert_offsets[E] = rows used
+ *   group_offsets[g]   = expert_offsets[g * E / G]  (group g = send buffer g)
+ *   row_src[r]         t * k + j of the pair stored in row r, -1 for pad rows
+ *   dst_row[t * k + j] row holding that pair, -1 if the slot is dropped
+ *   out[r]             x[t] (bf16 copy) or its E4M3 codes, scales[r][b] per
+ *                      128-channel block
+ * Rows at and beyond expert_offsets[E] are not written.
+ * Returns the number of rows used. */
+int64_t oracle_dispatch(const uint16_t* x, const int32_t* topk_idx,
+                        int64_t T, int H, int E, int k, int groups,
+                        int row_align, int fp8,
+                        void* out, float* scales,
+                        int32_t* expert_counts, int32_t* expert_offsets,
+                        int32_t* group_offsets, int32_t* row_src,
+                        int32_t* dst_row) {
+    const int64_t TK = T * (int64_t)k;
+    /* counts */
+    for (int e = 0; e < E; e++) expert_counts[e] = 0;
+    for (int64_t i = 0; i < TK; i++) {
+        int e = topk_idx[i];
+        if (e >= 0 && e < E) expert_counts[e]++;
+    }
+    /* padded counts -> offsets (exclusive running sum) */
+    expert_offsets[0] = 0;
+    for (int e = 0; e < E; e++) {
+        int64_t c = expert_counts[e];
+        int64_t padded = (c + row_align - 1) / row_align * row_align;
+        expert_offsets[e + 1] = (int32_t)(expert_offsets[e] + padded);
+    }
+    if (group_offsets) {
+        int per = E / groups;
+        for (int g = 0; g <= groups; g++) group_offsets[g] = expert_offsets[g * per];
+    }
+    /* stable placement: experts in order, tokens in order within an expert */
+    for (int64_t i = 0; i < TK; i++) dst_row[i] = -1;
+    for (int e = 0; e < E; e++) {
+        int64_t r = expert_offsets[e];
+        for (int64_t t = 0; t < T; t++)
+            for (int j = 0; j < k; j++)
+                if (topk_idx[t * k + j] == e) {
+                    dst_row[t * k + j] = (int32_t)r;
+                    row_src[r] = (int32_t)(t * k + j);
+                    r++;
+                }
+        for (; r < expert_offsets[e + 1]; r++) row_src[r] = -1;   /* pad rows */
+    }
+    /* payload */
+    const int nb = H / 128;
+    uint8_t* qrow = fp8 ? (uint8_t*)malloc((size_t)H) : NULL;
+    float* srow = fp8 ? (float*)malloc(sizeof(float) * (size_t)(nb > 0 ? nb : 1)) : NULL;
+    for (int64_t t = 0; t < T; t++) {
+        const uint16_t* xr = x + t * (int64_t)H;
+        if (fp8)
+            for (int b = 0; b < nb; b++)
+                oracle_quantize_block(xr + 128 * b, qrow + 128 * b, srow + b);
+        for (int j = 0; j < k; j++) {
+            int64_t r = dst_row[t * k + j];
+            if (r < 0) continue;
+            if (fp8) {
+                memcpy((uint8_t*)out + r * H, qrow, (size_t)H);
+                memcpy(scales + r * nb, srow, sizeof(float) * (size_t)nb);
+            } else {
+                memcpy((uint16_t*)out + r * H, xr, sizeof(uint16_t) * (size_t)H);
+            }
+        }
+    }
+    /* pad rows: zero payload and zero scales */
+    for (int e = 0; e < E; e++)
+        for (int64_t r = expert_offsets[e] + expert_counts[e]; r < expert_offsets[e + 1]; r++) {
+            if (fp8) {
+                memset((uint8_t*)out + r * H, 0, (size_t)H);
+                for (int b = 0; b < nb; b++) scales[r * nb + b] = 0.0f;
+            } else {
+                memset((uint16_t*)out + r * H, 0, sizeof(uint16_t) * (size_t)H);
+            }
+        }
+    free(qrow);
+    free(srow);
+    return expert_offsets[E];
+}
+
+/* ---------------------------------------------------------------- experts */
+
+/* Stand-in experts used around the path (not part of it): row r of expert e
+ * becomes bf16(fp32(v) * c_e) with c_e = fp32((e+1)/E), or c_e = 1 when
+ * identity is set; v is the bf16 row or, for FP8 rows, code value * scale in
+ * fp32. Pad rows become zero. Rows at and beyond num_rows are not written. */
+void oracle_expert_scale(const void* disp, const float* scales,
+                         const int32_t* row_src, const int32_t* topk_idx,
+                         int64_t num_rows, int H, int E, int fp8, int identity,
+                         uint16_t* expert_out) {
+    const int nb = H / 128;
+    for (int64_t r = 0; r < num_rows; r++) {
+        uint16_t* o = expert_out + r * H;
+        if (row_src[r] < 0) { memset(o, 0, sizeof(uint16_t) * (size_t)H); continue; }
+        int e = topk_idx[row_src[r]];
+        float c = identity ? 1.0f : (float)(e + 1) / (float)E;
+        for (int h = 0; h < H; h++) {
+            float v;
+            if (fp8) v = oracle_e4m3_value(((const uint8_t*)disp)[r * H + h]) * scales[r * nb + h / 128];
+            else v = bf16_value(((const uint16_t*)disp)[r * H + h]);
+            float prod = v * c;
+            o[h] = oracle_bf16_from_double((double)prod);
+        }
+    }
+}
+
+/* ---------------------------------------------------------------- combine */
+
+/* Weighted sum of each token's expert outputs with the router weights
+ * ([EPMC] Introduction: the final activation is the weighted average of the
+ * selected experts' outputs; Combine: the receiver reads each expert's row
+ * through the routing table and applies its weight; [EFA] Evaluation: the
+ * accumulation happens only on the receiving side). Accumulated in fp64 in
+ * slot order, rounded once to bf16. Dropped slots (dst_row < 0) add nothing. */
+void oracle_combine(const uint16_t* expert_out, const int32_t* dst_row,
+                    const float* topk_w, int64_t T, int H, int k, uint16_t* y) {
+    for (int64_t t = 0; t < T; t++)
+        for (int h = 0; h < H; h++) {
+            double acc = 0.0;
+            for (int j = 0; j < k; j++) {
+                int64_t r = dst_row[t * k + j];
+                if (r < 0) continue;
+                acc += (double)topk_w[t * k + j] * (double)bf16_value(expert_out[r * H + h]);
+            }
+            y[t * H + h] = oracle_bf16_from_double(acc);
+        }
+}
+
+/* ---------------------------------------------------------------- helpers */
+
+/* Elementwise encoders used by the tests that sweep the E4M3 rounding. */
+void oracle_e4m3_encode_array(const float* v, uint8_t* out, int64_t n) {
+    for (int64_t i = 0; i < n; i++) out[i] = oracle_e4m3_encode(v[i]);
+}
+
+void oracle_e4m3_encode_bits(uint32_t start, int64_t count, uint8_t* out) {
+    for (int64_t i = 0; i < count; i++) {
+        uint32_t u = start + (uint32_t)i;
+        float f;
+        memcpy(&f, &u, sizeof f);
+        out[i] = oracle_e4m3_encode(f);
+    }
+}
