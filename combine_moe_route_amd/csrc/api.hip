@@ -1,0 +1,170 @@
+// C ABI of libmoeroute: host-side argument checks, then kernel launches on the
+// caller's stream. No allocation, no global mutable state, no device->host
+// copies. Every check runs before the first HIP call, so invalid arguments
+// return an error without touching the GPU.
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "../../include/moe_route.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int64_t kInt32Max = 2147483647;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool log_enabled() {
+    static const int on = [] {
+        const char* v = getenv("MOE_ROUTE_LOG");
+        return (v && v[0] == '1') ? 1 : 0;
+    }();
+    return on != 0;
+}
+
+void log_launch(const char* what, const moe::LaunchInfo& i) {
+    fprintf(stderr, "[moe_route] %s grid=%lld block=%d lds=%zu param=%lld\n", what,
+            (long long)i.grid, i.block, i.lds, (long long)i.param);
+}
+
+int64_t max_rows_of(int64_t T, int E, int k, int row_align) {
+    if (T < 0 || k < 1 || E < k || E > MOE_MAX_EXPERTS || row_align < 1 || row_align > 1024)
+        return -1;
+    const int64_t tk = T * (int64_t)k;   // T < 2^62 is implied by the check below
+    if (T > kInt32Max) return -1;
+    const int64_t rows = tk + (int64_t)E * (row_align - 1);
+    return rows > kInt32Max ? -1 : rows;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+int moe_route_topk(const float* logits, int64_t T, int E, int k, int32_t* topk_idx,
+                   float* topk_w, void* stream) {
+    if (T < 0 || k < 1 || E < k || E > MOE_MAX_EXPERTS) return MOE_EINVAL;
+    if (T * (int64_t)k > kInt32Max || T * (int64_t)E > ((int64_t)1 << 40)) return MOE_EINVAL;
+    if (T == 0) return MOE_OK;
+    if (!logits || !topk_idx || !topk_w) return MOE_ENULL;
+    if (!aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4)) return MOE_EALIGN;
+    moe::LaunchInfo info;
+    const hipError_t e = moe::launch_route_topk(logits, T, E, k, topk_idx, topk_w,
+                                                static_cast<hipStream_t>(stream), &info);
+    if (log_enabled()) log_launch("route_topk", info);
+    return status_of(e);
+}
+
+int64_t moe_dispatch_max_rows(int64_t T, int E, int k, int row_align) {
+    return max_rows_of(T, E, k, row_align);
+}
+
+size_t moe_dispatch_workspace_bytes(int64_t T, int E, int k, int groups) {
+    if (max_rows_of(T, E, k, 1) < 0 || groups < 1 || E % groups != 0) return 0;
+    return (size_t)moe::dispatch_tiles(T) * (size_t)E * sizeof(int32_t);
+}
+
+int moe_dispatch(const void* x, const int32_t* topk_idx, int64_t T, int H, int E, int k,
+                 int groups, int row_align, int out_dtype, void* out, float* out_scales,
+                 int32_t* expert_counts, int32_t* expert_offsets, int32_t* group_offsets,
+                 int32_t* row_src, int32_t* dst_row, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+    // sizes and options
+    const int64_t max_rows = max_rows_of(T, E, k, row_align);
+    if (max_rows < 0) return MOE_EINVAL;
+    if (groups < 1 || groups > E || E % groups != 0) return MOE_EINVAL;
+    if (out_dtype != MOE_OUT_BF16 && out_dtype != MOE_OUT_FP8_E4M3) return MOE_EINVAL;
+    const bool fp8 = out_dtype == MOE_OUT_FP8_E4M3;
+    if (H < 1 || H > 65536 || H % (fp8 ? 128 : 8) != 0) return MOE_EINVAL;
+    // required pointers
+    if (!expert_counts || !expert_offsets) return MOE_ENULL;
+    if (T > 0 && (!x || !topk_idx || !dst_row)) return MOE_ENULL;
+    if (max_rows > 0 && (!out || !row_src)) return MOE_ENULL;
+    if (fp8 && max_rows > 0 && !out_scales) return MOE_ENULL;
+    // alignment
+    if (!aligned(x, 16) || !aligned(out, 16)) return MOE_EALIGN;
+    if (!aligned(topk_idx, 4) || !aligned(expert_counts, 4) || !aligned(expert_offsets, 4) ||
+        !aligned(group_offsets, 4) || !aligned(row_src, 4) || !aligned(dst_row, 4) ||
+        !aligned(workspace, 4) || (fp8 && !aligned(out_scales, 4)))
+        return MOE_EALIGN;
+    // workspace
+    const size_t need = moe_dispatch_workspace_bytes(T, E, k, groups);
+    if (workspace_bytes < need) return MOE_ENOSPC;
+    if (need > 0 && !workspace) return MOE_ENULL;
+
+    moe::DispatchArgs a;
+    a.x = x;
+    a.topk_idx = topk_idx;
+    a.T = T;
+    a.H = H;
+    a.E = E;
+    a.k = k;
+    a.groups = groups;
+    a.row_align = row_align;
+    a.fp8 = fp8;
+    a.out = out;
+    a.out_scales = out_scales;
+    a.expert_counts = expert_counts;
+    a.expert_offsets = expert_offsets;
+    a.group_offsets = group_offsets;
+    a.row_src = row_src;
+    a.dst_row = dst_row;
+    a.tile_counts = static_cast<int32_t*>(workspace);
+    a.max_rows = max_rows;
+    moe::LaunchInfo info[3];
+    const hipError_t e = moe::launch_dispatch(a, static_cast<hipStream_t>(stream), info);
+    if (log_enabled()) {
+        log_launch("dispatch.tile_hist", info[0]);
+        log_launch("dispatch.scan", info[1]);
+        log_launch("dispatch.scatter", info[2]);
+    }
+    return status_of(e);
+}
+
+int moe_combine(const void* expert_out, const int32_t* dst_row, const float* topk_w, int64_t T,
+                int H, int k, void* y, void* stream) {
+    if (T < 0 || k < 1 || k > MOE_MAX_EXPERTS || H < 1 || H > 65536 || H % 8 != 0)
+        return MOE_EINVAL;
+    if (T > kInt32Max || T * (int64_t)k > kInt32Max) return MOE_EINVAL;
+    if (T == 0) return MOE_OK;
+    if (!expert_out || !dst_row || !topk_w || !y) return MOE_ENULL;
+    if (!aligned(expert_out, 16) || !aligned(y, 16)) return MOE_EALIGN;
+    if (!aligned(dst_row, 4) || !aligned(topk_w, 4)) return MOE_EALIGN;
+    moe::LaunchInfo info;
+    const hipError_t e = moe::launch_combine(expert_out, dst_row, topk_w, T, H, k, y,
+                                             static_cast<hipStream_t>(stream), &info);
+    if (log_enabled()) log_launch("combine", info);
+    return status_of(e);
+}
+
+int moe_harness_expert_scale(const void* disp, const float* disp_scales, const int32_t* row_src,
+                             const int32_t* topk_idx, const int32_t* expert_offsets,
+                             int64_t max_rows, int H, int E, int out_dtype, int identity,
+                             void* expert_out, void* stream) {
+    if (max_rows < 0 || max_rows > kInt32Max || E < 1 || E > MOE_MAX_EXPERTS) return MOE_EINVAL;
+    if (out_dtype != MOE_OUT_BF16 && out_dtype != MOE_OUT_FP8_E4M3) return MOE_EINVAL;
+    const bool fp8 = out_dtype == MOE_OUT_FP8_E4M3;
+    if (H < 1 || H > 65536 || H % (fp8 ? 128 : 8) != 0) return MOE_EINVAL;
+    if (!expert_offsets) return MOE_ENULL;
+    if (max_rows == 0) return MOE_OK;
+    if (!disp || !row_src || !topk_idx || !expert_out || (fp8 && !disp_scales)) return MOE_ENULL;
+    if (!aligned(disp, 16) || !aligned(expert_out, 16)) return MOE_EALIGN;
+    return status_of(moe::launch_expert_scale(disp, disp_scales, row_src, topk_idx, expert_offsets,
+                                              max_rows, H, E, fp8, identity != 0, expert_out,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+const char* moe_status_string(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_EINVAL: return "invalid argument (size, count or option out of range)";
+        case MOE_ENOSPC: return "workspace smaller than moe_dispatch_workspace_bytes";
+        case MOE_EALIGN: return "pointer not aligned (16 bytes for payloads, 4 for the rest)";
+        case MOE_EHIP: return "HIP kernel launch failed";
+        case MOE_ENULL: return "required pointer is NULL";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,181 @@
+/*
+ * moe_route.h - MoE token routing, dispatch and combine on one MI355X (gfx950).
+ *
+ * A plain C ABI over hand-written HIP kernels. Every pointer argument named
+ * "device" is device memory owned by the caller; the library allocates
+ * nothing, keeps no global mutable state and only enqueues work on `stream`
+ * (a hipStream_t; NULL means the default stream). Nothing is copied back to
+ * the host: the number of rows dispatch produced stays on the device
+ * (expert_offsets[E]) and buffers are sized by capacity.
+ *
+ * The path, after the Perplexity posts "Efficient and portable
+ * mixture-of-experts communication" (sections Introduction, Dispatch,
+ * Combine) and "Enabling trillion-parameter models on AWS EFA" (sections Send
+ * and receive buffers, Dispatch and Combine, Evaluation), reduced to one GPU's
+ * share of the work:
+ *
+ *   logits --moe_route_topk--> topk_idx, topk_w
+ *   x, topk_idx --moe_dispatch--> per-expert contiguous rows (+ FP8 scales),
+ *                                 counts, offsets, group offsets, row maps
+ *   (experts run on the rows)
+ *   expert rows, dst_row, topk_w --moe_combine--> y
+ *
+ * Error behaviour: every function returns a moe_status. All argument checks
+ * run on the host before any HIP call, so an invalid call launches nothing
+ * and needs no GPU. MOE_EHIP reports a launch failure; faults inside kernels
+ * surface at the caller's next synchronisation. Values are not validated:
+ * logits must be finite, and each token's expert ids must be distinct.
+ * Calls on one stream are ordered; calls that share a workspace must not run
+ * concurrently on different streams.
+ */
+#ifndef MOE_ROUTE_H
+#define MOE_ROUTE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_EINVAL = -1,   /* a size, count or option is out of range */
+    MOE_ENOSPC = -2,   /* workspace smaller than moe_dispatch_workspace_bytes */
+    MOE_EALIGN = -3,   /* a pointer lacks the alignment stated below */
+    MOE_EHIP = -4,     /* a kernel launch failed */
+    MOE_ENULL = -5     /* a required pointer is NULL */
+} moe_status;
+
+typedef enum {
+    MOE_OUT_BF16 = 0,      /* dispatch rows are bf16 copies of x */
+    MOE_OUT_FP8_E4M3 = 1   /* dispatch rows are OCP E4M3 codes + 1x128 fp32 scales */
+} moe_out_dtype;
+
+/* Largest expert count the kernels accept. */
+#define MOE_MAX_EXPERTS 1024
+
+/*
+ * Router gate: per token, softmax over E logits, the k experts with the
+ * highest scores, and their probabilities renormalised over the chosen k
+ * ("Efficient and portable mixture-of-experts communication", Introduction:
+ * the router yields a probability distribution, the top-K experts are used
+ * and the output is a weighted average; the DeepSeek-V3 excerpts keep gating
+ * in its original precision, so this runs in fp32).
+ *
+ *   logits   device, fp32 [T, E] row-major, finite values, 4-byte aligned
+ *   topk_idx device, int32 [T, k] out: slot j holds the j-th best expert;
+ *            experts are ranked by logit, descending; equal logits (IEEE
+ *            equality, so -0 == +0) rank the lower expert index first
+ *   topk_w   device, fp32 [T, k] out: exp(l_j - l_max) / sum over the k
+ *            chosen of exp(l_i - l_max), which equals the softmax weight
+ *            renormalised over the chosen experts; k == 1 gives exactly 1
+ *   1 <= k <= E <= MOE_MAX_EXPERTS, T >= 0 (T == 0 is a no-op).
+ */
+int moe_route_topk(const float* logits, int64_t T, int E, int k,
+                   int32_t* topk_idx, float* topk_w, void* stream);
+
+/* Rows dispatch may use: T*k + E*(row_align-1); -1 if the arguments are
+ * invalid or the count does not fit in int32. */
+int64_t moe_dispatch_max_rows(int64_t T, int E, int k, int row_align);
+
+/* Workspace bytes moe_dispatch needs (per-tile expert counts); 0 on invalid
+ * arguments. The workspace holds no state between calls. */
+size_t moe_dispatch_workspace_bytes(int64_t T, int E, int k, int groups);
+
+/*
+ * Dispatch: count tokens per expert, turn the counts into segment offsets by
+ * an exclusive running sum, and pack every (token, slot) pair into its
+ * expert's contiguous segment ("Enabling trillion-parameter models on AWS
+ * EFA", Dispatch and Combine: per-expert counts, then their cumulative sum as
+ * the offsets for packing tokens into contiguous per-expert send buffers;
+ * "Efficient and portable mixture-of-experts communication", Dispatch:
+ * activations, block scales and the token index travel together and the
+ * source and token index are stored per row). Within a segment rows are in
+ * token order, so the layout is deterministic. With FP8, activations are
+ * scaled per token per 128 channels (DeepSeek-V3 excerpt on 1x128 tiles):
+ * s = amax / 448 in fp32, each code is the correctly rounded fp32 quotient
+ * x / s rounded to nearest-even E4M3 and saturated to +-448; an all-zero
+ * block has s = 0 and zero codes.
+ *
+ *   x              device, bf16 [T, H], 16-byte aligned
+ *   topk_idx       device, int32 [T, k]; an id outside [0, E) drops that slot
+ *                  (not counted, dst_row = -1, no row written)
+ *   T, H, E, k     1 <= k <= E <= MOE_MAX_EXPERTS; H % 8 == 0 (bf16) or
+ *                  H % 128 == 0 (FP8); 1 <= H <= 65536
+ *   groups         destination groups (1 = none), E % groups == 0; group g
+ *                  holds experts [g*E/groups, (g+1)*E/groups), so its rows
+ *                  form one contiguous send buffer
+ *   row_align      1..1024: every non-empty segment is padded to a multiple of
+ *                  this many rows; pad rows have zero payload, zero scales and
+ *                  row_src = -1 and sit at the end of the segment
+ *   out_dtype      moe_out_dtype
+ *   out            device [max_rows, H] bf16 or E4M3 bytes, 16-byte aligned
+ *   out_scales     device fp32 [max_rows, H/128] for FP8 (4-byte aligned),
+ *                  ignored for bf16
+ *   expert_counts  device int32 [E] out: pairs routed to each expert
+ *   expert_offsets device int32 [E+1] out: first row of each segment;
+ *                  expert_offsets[E] is the number of rows used
+ *   group_offsets  device int32 [groups+1] out, or NULL: first row of each
+ *                  group's send buffer
+ *   row_src        device int32 [max_rows] out: t*k+j of the pair in each
+ *                  row, -1 for pad rows
+ *   dst_row        device int32 [T, k] out: the row holding each pair
+ *   workspace      device, >= moe_dispatch_workspace_bytes, 4-byte aligned
+ * Rows at and beyond expert_offsets[E] are left untouched. max_rows is
+ * moe_dispatch_max_rows(T, E, k, row_align). T == 0 writes zero counts and
+ * offsets.
+ */
+int moe_dispatch(const void* x, const int32_t* topk_idx,
+                 int64_t T, int H, int E, int k, int groups, int row_align,
+                 int out_dtype, void* out, float* out_scales,
+                 int32_t* expert_counts, int32_t* expert_offsets,
+                 int32_t* group_offsets, int32_t* row_src, int32_t* dst_row,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Combine: each token's output is the weighted sum of the rows its experts
+ * produced, y[t] = bf16(sum_j topk_w[t,j] * expert_out[dst_row[t,j]]),
+ * accumulated in fp32 in slot order and rounded once to bf16 (nearest even).
+ * This is the receiving side's weighted average ("Efficient and portable
+ * mixture-of-experts communication", Combine: the routing table gives the
+ * buffer to read and the weight of each expert; "Enabling trillion-parameter
+ * models on AWS EFA", Evaluation: accumulation only on the receiving side;
+ * the DeepSeek-V3 excerpts keep combine in BF16).
+ *
+ *   expert_out  device bf16 [rows, H], 16-byte aligned; rows named by dst_row
+ *   dst_row     device int32 [T, k]; a negative entry contributes nothing
+ *   topk_w      device fp32 [T, k]
+ *   y           device bf16 [T, H] out, 16-byte aligned
+ *   H % 8 == 0, 1 <= H <= 65536, 1 <= k <= MOE_MAX_EXPERTS, T >= 0.
+ */
+int moe_combine(const void* expert_out, const int32_t* dst_row,
+                const float* topk_w, int64_t T, int H, int k,
+                void* y, void* stream);
+
+/*
+ * Stand-in experts for tests and the benchmark (not part of the path):
+ * expert_out[r] = bf16(v * c_e) with c_e = fp32(e+1) / fp32(E) (or 1 when
+ * identity != 0), e the expert of row r, v the bf16 row or, for FP8 rows,
+ * the code's value times its block scale in fp32. Pad rows become zero. Rows
+ * from expert_offsets[E] up to max_rows are not written.
+ *
+ *   disp, disp_scales  moe_dispatch's out / out_scales
+ *   row_src, topk_idx  moe_dispatch's row_src and its topk_idx input
+ *   expert_offsets     moe_dispatch's expert_offsets
+ *   expert_out         device bf16 [max_rows, H] out, 16-byte aligned
+ */
+int moe_harness_expert_scale(const void* disp, const float* disp_scales,
+                             const int32_t* row_src, const int32_t* topk_idx,
+                             const int32_t* expert_offsets, int64_t max_rows,
+                             int H, int E, int out_dtype, int identity,
+                             void* expert_out, void* stream);
+
+/* Static text for a status code. */
+const char* moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_ROUTE_H */

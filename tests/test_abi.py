@@ -1,0 +1,164 @@
+"""The C ABI loads, exports every symbol include/moe_route.h declares, and
+rejects invalid arguments on the host before any HIP call (so these run
+without a GPU). No test here launches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_route.h")
+
+binding = pytest.importorskip("combine_moe_route_amd.binding")
+lib = binding.lib
+
+OK, EINVAL, ENOSPC, EALIGN, EHIP, ENULL = 0, -1, -2, -3, -4, -5
+A = 0x100000      # fake device addresses: never dereferenced, validation fails first
+B = 0x200000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert len(names) >= 6
+    raw = ctypes.CDLL(binding.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+    assert sorted(binding.EXPORTS) == names
+
+
+def test_header_status_codes_match_binding():
+    text = open(HEADER).read()
+    for name, val in [("MOE_OK", OK), ("MOE_EINVAL", EINVAL), ("MOE_ENOSPC", ENOSPC),
+                      ("MOE_EALIGN", EALIGN), ("MOE_EHIP", EHIP), ("MOE_ENULL", ENULL)]:
+        assert re.search(rf"\b{name}\s*=\s*{val}\b", text), name
+        assert getattr(binding, name) == val
+    assert re.search(r"MOE_MAX_EXPERTS\s+1024", text)
+
+
+def test_status_strings():
+    for s in (OK, EINVAL, ENOSPC, EALIGN, EHIP, ENULL):
+        assert binding.status_string(s) and binding.status_string(s) != "unknown status"
+    assert binding.status_string(7) == "unknown status"
+
+
+def test_max_rows_and_workspace():
+    assert lib.moe_dispatch_max_rows(16384, 256, 8, 128) == 16384 * 8 + 256 * 127
+    assert lib.moe_dispatch_max_rows(4096, 384, 8, 1) == 4096 * 8
+    assert lib.moe_dispatch_max_rows(0, 4, 2, 1) == 0
+    assert lib.moe_dispatch_max_rows(10, 4, 5, 1) == -1          # k > E
+    assert lib.moe_dispatch_max_rows(10, 1025, 2, 1) == -1       # E too large
+    assert lib.moe_dispatch_max_rows(10, 4, 2, 0) == -1          # row_align < 1
+    assert lib.moe_dispatch_max_rows(10, 4, 2, 1025) == -1
+    assert lib.moe_dispatch_max_rows(2 ** 28, 8, 8, 1) == -1     # rows overflow int32
+    assert lib.moe_dispatch_workspace_bytes(16384, 256, 8, 32) == 64 * 256 * 4
+    assert lib.moe_dispatch_workspace_bytes(300, 8, 2, 1) == 2 * 8 * 4
+    assert lib.moe_dispatch_workspace_bytes(0, 8, 2, 1) == 0
+    assert lib.moe_dispatch_workspace_bytes(300, 8, 2, 3) == 0   # E % groups != 0
+
+
+def route(logits=A, T=16, E=8, k=2, idx=B, w=B + 4096):
+    return lib.moe_route_topk(logits, T, E, k, idx, w, None)
+
+
+def test_route_topk_validation():
+    assert route(k=0) == EINVAL
+    assert route(k=9) == EINVAL
+    assert route(E=1025, k=2) == EINVAL
+    assert route(T=-1) == EINVAL
+    assert route(T=2 ** 31, k=2) == EINVAL
+    assert route(logits=None) == ENULL
+    assert route(idx=None) == ENULL
+    assert route(logits=A + 2) == EALIGN
+    assert route(T=0, logits=None, idx=None, w=None) == OK      # no-op
+
+
+def dispatch(**kw):
+    a = dict(x=A, idx=B, T=256, H=256, E=8, k=2, groups=1, row_align=1, dt=0, out=A + 2 ** 20,
+             scales=A + 2 ** 21, counts=B + 2 ** 20, offsets=B + 2 ** 20 + 64,
+             goff=B + 2 ** 20 + 128, row_src=B + 2 ** 21, dst_row=B + 2 ** 22,
+             ws=B + 2 ** 23, wsb=1 << 20)
+    a.update(kw)
+    return lib.moe_dispatch(a["x"], a["idx"], a["T"], a["H"], a["E"], a["k"], a["groups"],
+                            a["row_align"], a["dt"], a["out"], a["scales"], a["counts"],
+                            a["offsets"], a["goff"], a["row_src"], a["dst_row"], a["ws"], a["wsb"],
+                            None)
+
+
+def test_dispatch_validation():
+    assert dispatch(k=0) == EINVAL
+    assert dispatch(k=9) == EINVAL
+    assert dispatch(E=2000) == EINVAL
+    assert dispatch(groups=3) == EINVAL                  # 8 % 3 != 0
+    assert dispatch(groups=0) == EINVAL
+    assert dispatch(groups=16) == EINVAL                 # more groups than experts
+    assert dispatch(row_align=0) == EINVAL
+    assert dispatch(row_align=2048) == EINVAL
+    assert dispatch(dt=2) == EINVAL
+    assert dispatch(H=12) == EINVAL                      # bf16 rows need H % 8 == 0
+    assert dispatch(H=200, dt=1) == EINVAL               # FP8 rows need H % 128 == 0
+    assert dispatch(H=0) == EINVAL
+    assert dispatch(H=65544) == EINVAL
+    assert dispatch(T=-5) == EINVAL
+    assert dispatch(T=2 ** 29, k=8) == EINVAL            # rows overflow int32
+    assert dispatch(x=None) == ENULL
+    assert dispatch(idx=None) == ENULL
+    assert dispatch(out=None) == ENULL
+    assert dispatch(row_src=None) == ENULL
+    assert dispatch(dst_row=None) == ENULL
+    assert dispatch(counts=None) == ENULL
+    assert dispatch(offsets=None) == ENULL
+    assert dispatch(dt=1, scales=None) == ENULL
+    assert dispatch(ws=None) == ENULL
+    assert dispatch(x=A + 8) == EALIGN                   # payloads need 16 bytes
+    assert dispatch(out=A + 2 ** 20 + 4) == EALIGN
+    assert dispatch(idx=B + 2) == EALIGN
+    assert dispatch(dst_row=B + 2 ** 22 + 1) == EALIGN
+    assert dispatch(wsb=7) == ENOSPC
+    assert dispatch(wsb=lib.moe_dispatch_workspace_bytes(256, 8, 2, 1) - 4) == ENOSPC
+
+
+def test_combine_validation():
+    c = lambda eo=A, dr=B, w=B + 4096, T=16, H=64, k=2, y=A + 2 ** 20: lib.moe_combine(
+        eo, dr, w, T, H, k, y, None)
+    assert c(H=60) == EINVAL
+    assert c(H=0) == EINVAL
+    assert c(k=0) == EINVAL
+    assert c(k=1025) == EINVAL
+    assert c(T=-1) == EINVAL
+    assert c(eo=None) == ENULL
+    assert c(y=None) == ENULL
+    assert c(eo=A + 8) == EALIGN
+    assert c(y=A + 2 ** 20 + 2) == EALIGN
+    assert c(w=B + 4098) == EALIGN
+    assert c(T=0, eo=None, dr=None, w=None, y=None) == OK
+
+
+def test_harness_validation():
+    h = lambda **kw: lib.moe_harness_expert_scale(
+        kw.get("disp", A), kw.get("sc", B), kw.get("rs", B + 4096), kw.get("idx", B + 8192),
+        kw.get("off", B + 16384), kw.get("R", 100), kw.get("H", 256), kw.get("E", 8),
+        kw.get("dt", 0), 0, kw.get("eo", A + 2 ** 20), None)
+    assert h(H=100) == EINVAL
+    assert h(dt=1, H=64) == EINVAL
+    assert h(E=0) == EINVAL
+    assert h(dt=3) == EINVAL
+    assert h(off=None) == ENULL
+    assert h(dt=1, sc=None) == ENULL
+    assert h(disp=A + 4) == EALIGN
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    import subprocess
+    import sys
+    code = ("import os; os.environ['MOE_ROUTE_LIB']=%r\n"
+            "try:\n import combine_moe_route_amd\nexcept ImportError as e:\n print('IMPORTERROR', e)\n"
+            % str(tmp_path / "missing.so"))
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True)
+    assert "IMPORTERROR" in r.stdout and "libmoeroute.so not found" in r.stdout

@@ -1,0 +1,242 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Routing indices, counts, offsets, group offsets, both row maps, bf16 rows,
+FP8 codes and scales must match bit for bit; router weights within 1e-5
+relative; combine within |gpu - oracle| <= 1e-2 * max(1, |oracle|) (and, as
+a tighter internal check, within one bf16 unit).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from moe_synth import WORKLOADS, bf16_bits_to_f32, f32_to_bf16_bits, gen_logits, gen_x_bf16
+from parity_util import (Case, bf16_to_np, combine_within_tolerance, dispatch_parity,
+                         experts_and_combine_parity, full_case, log, route_parity, to_dev_bf16)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    import combine_moe_route_amd  # noqa: F401  (raises if the HIP library is missing)
+    return torch.device("cuda:0")
+
+
+def case_of(name, **kw):
+    w = WORKLOADS[name]
+    d = dict(T=w.T, H=w.H, E=w.E, k=w.k, groups=w.groups, row_align=w.row_align, fp8=w.fp8,
+             seed=w.seed, zipf_s=w.zipf_s)
+    d.update(kw)
+    return Case(**d)
+
+
+# ----------------------------------------------------------------- the five workloads
+
+@pytest.mark.parametrize("name", ["tiny", "mixtral_decode", "dsv3_decode"])
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_decode_workloads_full_parity(dev, name, seed):
+    r = full_case(case_of(name, seed=seed), dev)
+    log(f"  combine bit-exact fraction {r['exact']:.5f}")
+
+
+def test_kimi_prefill_full_parity(dev):
+    r = full_case(case_of("kimi_prefill"), dev)
+    counts = r["ref"].expert_counts
+    log(f"  skew: hottest expert {counts.max()} of {r['ref'].num_rows} rows, "
+        f"{int(np.sum(counts == 0))} empty; combine exact {r['exact']:.5f}")
+
+
+def test_dsv3_prefill_full_size(dev):
+    """Full 16384-token FP8 workload: routing and the whole dispatch layout and
+    payload bit for bit; stand-in experts and combine on a token sample."""
+    from combine_moe_route_amd import moe_combine, moe_harness_expert_scale, moe_route_topk
+    c = case_of("dsv3_prefill")
+    log(f"[case] {c.label()}")
+    x_np = gen_x_bf16(c.T, c.H, c.seed)
+    logits = gen_logits(c.T, c.E, c.seed)
+    idx_np, w_np = route_parity(logits, c.k, dev)
+    ref, bufs = dispatch_parity(x_np, idx_np, c.E, c.groups, c.row_align, c.fp8, dev)
+    assert ref.num_rows == 147584
+    # experts on the GPU for every row; oracle experts on the rows of a sample
+    idx = torch.from_numpy(idx_np).to(dev)
+    eo = moe_harness_expert_scale(bufs, idx, c.E, fp8=True)
+    rng = np.random.default_rng(0)
+    toks = np.sort(rng.choice(c.T, 384, replace=False))
+    rows = np.unique(ref.dst_row[toks].ravel())
+    sub = oracle.Dispatch(ref.out[rows], ref.scales[rows], ref.expert_counts, ref.expert_offsets,
+                          ref.group_offsets, ref.row_src[rows], ref.dst_row, len(rows))
+    eo_ref = oracle.expert_scale(sub, idx_np, c.E, fp8=True)
+    rows_t = torch.from_numpy(rows.astype(np.int64)).to(dev)
+    assert np.array_equal(bf16_to_np(eo[rows_t]), eo_ref)
+    y = moe_combine(eo, bufs.dst_row, torch.from_numpy(w_np).to(dev))
+    remap = np.searchsorted(rows, ref.dst_row[toks])
+    y_ref = oracle.combine(eo_ref, remap.astype(np.int32), w_np[toks])
+    ok, within_ulp, exact = combine_within_tolerance(bf16_to_np(y[torch.from_numpy(toks).to(dev)]), y_ref)
+    assert ok.all() and within_ulp.all()
+    log(f"  combine exact on sample {exact:.5f}")
+
+
+# ----------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("c", [
+    Case(T=300, H=136, E=8, k=2, seed=1),                       # ragged tile, 17 units per row
+    Case(T=257, H=384, E=16, k=4, groups=4, row_align=8, fp8=True, seed=2),  # ragged, 24 units
+    Case(T=1, H=128, E=4, k=4, groups=2, row_align=128, fp8=True),
+    Case(T=1, H=8, E=1, k=1),                                   # smallest everything
+    Case(T=513, H=64, E=8, k=8, seed=3),                        # k == E
+    Case(T=200, H=256, E=65, k=5, seed=4),                      # two logits per lane
+    Case(T=100, H=128, E=1024, k=3, groups=1024, seed=5),       # largest E, G == E
+    Case(T=600, H=512, E=384, k=8, zipf_s=1.1, seed=6),         # skew, many empty experts
+    Case(T=100, H=256, E=16, k=12, row_align=1024, seed=7),     # k > 8, biggest padding
+    Case(T=3, H=65536, E=4, k=2, seed=8),                       # longest row
+    Case(T=2048, H=1024, E=256, k=8, groups=32, row_align=128, fp8=True, seed=9),
+], ids=lambda c: c.label())
+def test_edge_shapes(dev, c):
+    full_case(c, dev)
+
+
+def test_identity_experts_round_trip(dev):
+    for fp8 in (False, True):
+        r = full_case(Case(T=256, H=512, E=32, k=4, groups=4, row_align=16 if fp8 else 1,
+                           fp8=fp8, seed=11), dev, identity=True)
+        y = bf16_bits_to_f32(bf16_to_np(r["y"])).astype(np.float64)
+        x = bf16_bits_to_f32(r["x"]).astype(np.float64)
+        if fp8:
+            amax = np.abs(x).reshape(x.shape[0], -1, 128).max(-1).repeat(128, axis=1)
+            assert np.all(np.abs(y - x) <= 2 ** -4 * np.abs(x) + 2 ** -10 * amax / 448 + 2 ** -7 * np.abs(x))
+        else:
+            assert np.all(np.abs(y - x) <= np.spacing(np.abs(x).astype(np.float32)) * 2 ** 16)
+
+
+def test_k1_combine_returns_expert_row_bitwise(dev):
+    r = full_case(Case(T=300, H=256, E=8, k=1, seed=12), dev)
+    assert np.array_equal(bf16_to_np(r["y"]), r["y_ref"])
+
+
+def test_router_ties_and_signed_zero(dev):
+    rng = np.random.default_rng(13)
+    for E, k in [(8, 2), (64, 8), (256, 8), (384, 8), (1000, 16)]:
+        l = (np.round(rng.standard_normal((300, E)) * 2) / 4).astype(np.float32)
+        l[0] = 0.0
+        l[1, ::2] = -0.0
+        l[2] = 1.25
+        idx, w = route_parity(l, k, dev)
+        assert np.allclose(w[2], 1.0 / k)
+
+
+def test_all_tokens_one_expert_and_dropped_slots(dev):
+    T, E, k = 1000, 8, 3
+    idx = np.zeros((T, k), np.int32)
+    idx[:, 1] = 5
+    idx[:, 2] = np.where(np.arange(T) % 3 == 0, -1, 7)           # dropped every third
+    idx[::7, 2] = E                                               # out of range: dropped
+    full_case(Case(T=T, H=256, E=E, k=k, groups=2, row_align=4, seed=14), dev, idx_np=idx)
+    full_case(Case(T=T, H=256, E=E, k=k, groups=2, row_align=128, fp8=True, seed=14), dev, idx_np=idx)
+
+
+def test_zero_tokens_writes_empty_layout(dev):
+    from combine_moe_route_amd import moe_combine, moe_dispatch, moe_route_topk
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device=dev)
+    idx = torch.empty((0, 2), dtype=torch.int32, device=dev)
+    bufs = moe_dispatch(x, idx, 8, groups=4, row_align=128, fp8=True)
+    i, w = moe_route_topk(torch.empty((0, 8), device=dev), 2)
+    y = moe_combine(torch.empty((8 * 127, 256), dtype=torch.bfloat16, device=dev), bufs.dst_row, w)
+    torch.cuda.synchronize()
+    assert bufs.expert_counts.cpu().tolist() == [0] * 8
+    assert bufs.expert_offsets.cpu().tolist() == [0] * 9
+    assert bufs.group_offsets.cpu().tolist() == [0] * 5
+    assert y.shape == (0, 256) and i.shape == (0, 2)
+
+
+def test_zero_blocks_and_negative_zero_fp8(dev):
+    T, H, E, k = 64, 512, 4, 2
+    x = gen_x_bf16(T, H, 15)
+    x[0] = 0                          # whole row zero
+    x[1, :128] = 0x8000               # a block of -0.0
+    x[2, 5] = 0x8000
+    x[3, 128:256] = f32_to_bf16_bits(np.full(128, 1e-38, np.float32))   # tiny block
+    x[4, 256:384] = f32_to_bf16_bits(np.full(128, 3e38, np.float32))    # huge block
+    idx, _ = oracle.route_topk(gen_logits(T, E, 15), k)
+    dispatch_parity(x, idx, E, 2, 8, True, dev)
+
+
+def test_repeat_runs_bit_identical(dev):
+    from combine_moe_route_amd import moe_combine, moe_dispatch, moe_route_topk
+    c = case_of("dsv3_decode", T=1500)
+    x = to_dev_bf16(gen_x_bf16(c.T, c.H, 16), dev)
+    logits = torch.from_numpy(gen_logits(c.T, c.E, 16)).to(dev)
+    first = None
+    for it in range(20):
+        i, w = moe_route_topk(logits, c.k)
+        b = moe_dispatch(x, i, c.E, c.groups, 128, True)
+        eo = torch.zeros((b.out.shape[0], c.H), dtype=torch.bfloat16, device=dev)
+        R = int(b.expert_offsets[-1])
+        eo[:R] = b.out[:R].view(torch.float8_e4m3fn).float().to(torch.bfloat16)
+        y = moe_combine(eo, b.dst_row, w)
+        cur = [i.clone(), w.clone(), b.out[:R].clone(), b.out_scales[:R].clone(), b.row_src[:R].clone(),
+               b.dst_row.clone(), y.clone()]
+        cur = [t.contiguous().view(torch.uint8) for t in cur]
+        if first is None:
+            first = cur
+        else:
+            for a, bb in zip(first, cur):
+                assert torch.equal(a, bb), f"run {it} differs"
+
+
+def _fp8_domain_rows(amax_bits: np.ndarray, rng, per_amax_blocks: int):
+    """Blocks whose first element is the block maximum and whose other 127
+    elements are bf16 values drawn uniformly over the bit patterns below it."""
+    blocks = []
+    for a in amax_bits:
+        vals = rng.integers(0, int(a) + 1, size=(per_amax_blocks, 127), dtype=np.int64).astype(np.uint16)
+        sign = rng.integers(0, 2, size=vals.shape).astype(np.uint16) << 15
+        b = np.concatenate([np.full((per_amax_blocks, 1), a, np.uint16), vals | sign], axis=1)
+        blocks.append(b)
+    return np.concatenate(blocks)
+
+
+def test_fp8_quantiser_domain_sweep(dev):
+    """The FP8 element path over the (x, amax) domain: every bf16 binade of the
+    block maximum (normal and subnormal), x spread over all smaller patterns."""
+    rng = np.random.default_rng(17)
+    amax = np.concatenate([
+        np.arange(1, 128, dtype=np.uint16),                       # subnormal amax
+        (np.arange(1, 255, dtype=np.uint16) << 7) | 0,            # every exponent, mantissa 0
+        (np.arange(1, 255, dtype=np.uint16) << 7) | 0x55,
+        (np.arange(1, 255, dtype=np.uint16) << 7) | 0x7F,
+        rng.integers(0x0080, 0x7F80, 512).astype(np.uint16),
+    ])
+    blocks = _fp8_domain_rows(amax, rng, 16)
+    H = 1024
+    n = blocks.shape[0] // (H // 128) * (H // 128)
+    x = blocks[:n].reshape(-1, H)
+    idx = np.zeros((x.shape[0], 1), np.int32)
+    log(f"  sweep: {x.size} elements, {n} blocks")
+    dispatch_parity(x, idx, 1, 1, 1, True, dev)
+
+
+@pytest.mark.slow
+def test_fp8_quantiser_exhaustive_domain(dev):
+    """Every (x, amax) bf16 pair with |x| <= amax, amax > 0 (~2^30 pairs)."""
+    H = 4096
+    chunk = []
+    done = 0
+    for a in range(1, 0x7F80):
+        mags = np.arange(0, a + 1, dtype=np.uint32)
+        vals = np.concatenate([mags, mags[1:] | 0x8000]).astype(np.uint16)
+        pad = (-len(vals)) % 127
+        vals = np.concatenate([vals, np.zeros(pad, np.uint16)]).reshape(-1, 127)
+        chunk.append(np.concatenate([np.full((len(vals), 1), a, np.uint16), vals], axis=1))
+        if sum(len(c) for c in chunk) >= (1 << 18) or a == 0x7F7F:
+            b = np.concatenate(chunk)
+            if a == 0x7F7F:   # pad the last rows with all-zero blocks
+                b = np.concatenate([b, np.zeros(((-len(b)) % (H // 128), 128), np.uint16)])
+            n = len(b) // (H // 128) * (H // 128)
+            rest = b[n:]
+            x = b[:n].reshape(-1, H)
+            dispatch_parity(x, np.zeros((x.shape[0], 1), np.int32), 1, 1, 1, True, dev)
+            done += n
+            chunk = [rest] if len(rest) else []
+            log(f"  exhaustive: amax up to {a:#06x}, {done} blocks")
