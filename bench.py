@@ -1,0 +1,276 @@
+"""Benchmark of the MoE dispatch + combine path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3_prefill]
+
+One step = route (top-k) + dispatch (counts, scan, scatter/FP8) + combine
+over one batch of the workload's synthetic inputs, all resident in HBM. The
+stand-in experts run once before timing (they are not part of the path).
+Before every step a 1 GiB scratch buffer is written so the step starts with
+a cold Infinity Cache; that write is outside the timed events. Dispatch and
+combine are timed with HIP events on the stream the kernels are launched on.
+
+Prints one JSON line. value = effective HBM GB/s = algorithmic bytes of
+dispatch + combine / (dispatch + combine time), median over steps.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+COMBINE_SRC = os.path.join(ROOT, "combine_moe_route_amd", "csrc", "combine.hip")
+SCATTER_SRC = os.path.join(ROOT, "combine_moe_route_amd", "csrc", "dispatch.hip")
+
+
+def algorithmic_bytes(T, H, E, k, R, fp8):
+    """Bytes the method must move (no re-reads, no workspace).
+
+    dispatch: logits 4TE + x 2TH + payload R*H*b (pad rows included)
+              + scales 4R*H/128 (FP8) + topk_idx/topk_w/dst_row 12Tk + row_src 4R
+    combine:  gathered rows 2Tk*H + y 2TH + dst_row/topk_w 8Tk
+    """
+    b = 1 if fp8 else 2
+    d = 4 * T * E + 2 * T * H + R * H * b + (4 * R * (H // 128) if fp8 else 0) + 12 * T * k + 4 * R
+    c = 2 * T * k * H + 2 * T * H + 8 * T * k
+    return d, c
+
+
+def src_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic(kernel_tag, workload, src_path):
+    """HBM traffic per launch from a committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    p = os.path.join(PROFILES, f"{kernel_tag}_{workload}_counters.md")
+    if not os.path.exists(p):
+        return None
+    text = open(p).read()
+    m = re.search(r"source_sha256_16:\s*([0-9a-f]{16})", text)
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != src_hash(src_path):
+        return None
+    return float(t.group(1))
+
+
+def pct(a, q):
+    return float(np.percentile(np.asarray(a), q))
+
+
+def run_gpu(w, steps, warmup, cold=True):
+    import torch
+
+    from combine_moe_route_amd import (alloc_dispatch, moe_combine, moe_dispatch,
+                                       moe_dispatch_max_rows, moe_harness_expert_scale,
+                                       moe_route_topk)
+    from moe_synth import gen_inputs
+
+    dev = torch.device("cuda:0")
+    x_np, l_np = gen_inputs(w)
+    x = torch.from_numpy(x_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    logits = torch.from_numpy(l_np).to(dev)
+    topk_idx = torch.empty((w.T, w.k), dtype=torch.int32, device=dev)
+    topk_w = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
+    bufs = alloc_dispatch(w.T, w.H, w.E, w.k, w.groups, w.row_align, w.fp8, dev)
+    y = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev)
+    cap = moe_dispatch_max_rows(w.T, w.E, w.k, w.row_align)
+    expert_out = torch.empty((cap, w.H), dtype=torch.bfloat16, device=dev)
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    # stand-in experts once (outside the path, untimed)
+    moe_route_topk(logits, w.k, topk_idx, topk_w)
+    moe_dispatch(x, topk_idx, w.E, w.groups, w.row_align, w.fp8, bufs)
+    moe_harness_expert_scale(bufs, topk_idx, w.E, w.fp8, expert_out=expert_out)
+    torch.cuda.synchronize()
+    R = int(bufs.expert_offsets[-1].item())
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+
+    def step(e=None):
+        if cold:
+            scratch.fill_(1)
+        if e is not None:
+            e[0].record(stream)
+        moe_route_topk(logits, w.k, topk_idx, topk_w)
+        if e is not None:
+            e[1].record(stream)
+        moe_dispatch(x, topk_idx, w.E, w.groups, w.row_align, w.fp8, bufs)
+        if e is not None:
+            e[2].record(stream)
+        moe_combine(expert_out, bufs.dst_row, topk_w, y)
+        if e is not None:
+            e[3].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    route = [a[0].elapsed_time(a[1]) * 1e3 for a in ev]       # microseconds
+    disp = [a[1].elapsed_time(a[2]) * 1e3 for a in ev]
+    comb = [a[2].elapsed_time(a[3]) * 1e3 for a in ev]
+    return dict(R=R, route=route, disp=disp, comb=comb, wall_s=wall)
+
+
+def copy_bandwidth(nbytes=1 << 30, reps=10):
+    """Device-to-device copy bandwidth (read + write bytes / time)."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(3)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    return 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
+def cpu_baseline(w, max_tokens):
+    """The CPU oracle (single thread, as it stands) on a bounded token sample of
+    the same workload: routing + dispatch + combine; its experts are replaced by
+    the token rows themselves (identity) so no oracle time goes to them."""
+    import oracle
+    from moe_synth import gen_inputs
+    ws = w.with_(T=min(w.T, max_tokens))
+    x, l = gen_inputs(ws)
+    t0 = time.perf_counter()
+    idx, wt = oracle.route_topk(l, ws.k)
+    d = oracle.dispatch(x, idx, ws.E, ws.groups, ws.row_align, ws.fp8)
+    t1 = time.perf_counter()
+    eo = np.ascontiguousarray(x[np.maximum(d.row_src, 0) // ws.k])
+    t2 = time.perf_counter()
+    oracle.combine(eo, d.dst_row, wt)
+    t3 = time.perf_counter()
+    bd, bc = algorithmic_bytes(ws.T, ws.H, ws.E, ws.k, d.num_rows, ws.fp8)
+    secs = (t1 - t0) + (t3 - t2)
+    return dict(value=round((bd + bc) / secs / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
+                sample=(f"{ws.T} of {w.T} tokens of {w.name} (H={ws.H}, E={ws.E}, k={ws.k}), "
+                        f"single-threaded C oracle, route+dispatch {t1 - t0:.2f} s, "
+                        f"combine {t3 - t2:.2f} s"),
+                seconds=round(secs, 3))
+
+
+def summarize(w, r):
+    bd, bc = algorithmic_bytes(w.T, w.H, w.E, w.k, r["R"], w.fp8)
+    tot = [a + b + c for a, b, c in zip(r["route"], r["disp"], r["comb"])]
+    dmed = statistics.median([a + b for a, b in zip(r["route"], r["disp"])])
+    cmed = statistics.median(r["comb"])
+    tmed = statistics.median(tot)
+    return dict(
+        bytes_dispatch=bd, bytes_combine=bc, rows=r["R"],
+        us_route=round(statistics.median(r["route"]), 2),
+        us_dispatch=round(dmed, 2), us_combine=round(cmed, 2), us_total=round(tmed, 2),
+        us_total_p10=round(pct(tot, 10), 2), us_total_p90=round(pct(tot, 90), 2),
+        gbps=round((bd + bc) / (tmed * 1e-6) / 1e9, 1),
+        gbps_dispatch=round(bd / (dmed * 1e-6) / 1e9, 1),
+        gbps_combine=round(bc / (cmed * 1e-6) / 1e9, 1),
+        pct_of_peak=round(100 * (bd + bc) / (tmed * 1e-6) / 1e9 / PEAK_HBM_GBPS, 2),
+    )
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsv3_prefill")
+    ap.add_argument("--also", default="kimi_prefill",
+                    help="comma-separated extra workloads reported under 'other' ('' for none)")
+    ap.add_argument("--warm", action="store_true", help="skip the cache flush between steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=16384)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="only run 1 GiB device copies (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this path runs on one GPU; multi-GPU runs are not part of it "
+                                   "(see the sharding note in DESIGN.md)", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    from moe_synth import WORKLOADS
+
+    if args.calib_copy:
+        print(json.dumps({"copy_GBps": round(copy_bandwidth(), 1), "bytes_per_copy": 1 << 30}),
+              flush=True)
+        return
+
+    w = WORKLOADS[args.workload]
+    print(f"[bench] {w.name}: T={w.T} H={w.H} E={w.E} k={w.k} G={w.groups} A={w.row_align} "
+          f"fp8={w.fp8} steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
+    r = run_gpu(w, args.steps, args.warmup, cold=not args.warm)
+    s = summarize(w, r)
+    print(f"[bench] {json.dumps(s)}", file=sys.stderr, flush=True)
+
+    others = {}
+    for name in [n for n in args.also.split(",") if n and n != w.name]:
+        wo = WORKLOADS[name]
+        print(f"[bench] {name}", file=sys.stderr, flush=True)
+        others[name] = summarize(wo, run_gpu(wo, args.steps, args.warmup, cold=not args.warm))
+    copy_gbps = round(copy_bandwidth(), 1)
+
+    comb_avg_us = statistics.mean(r["comb"])
+    achieved = s["bytes_combine"] / (comb_avg_us * 1e-6) / 1e9
+    traffic = read_traffic("combine", w.name, COMBINE_SRC)
+
+    out = {
+        "metric": "dispatch+combine µs and effective HBM GB/s (% of peak), 1 MI355X",
+        "value": s["gbps"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(s["us_total"] / 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 dispatch / bf16 combine, fp32 math" if w.fp8 else "bf16, fp32 math",
+        "data": "synthetic (seeded numpy; x~N(0,1) bf16, logits~N(0,1) fp32)",
+        "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "k": w.k,
+                   "groups": w.groups, "row_align": w.row_align,
+                   "cache": "warm" if args.warm else "cold (1 GiB write before each step)"},
+        "us_dispatch": s["us_dispatch"], "us_route": s["us_route"],
+        "us_combine": s["us_combine"], "us_total": s["us_total"],
+        "us_total_p10": s["us_total_p10"], "us_total_p90": s["us_total_p90"],
+        "pct_of_peak": s["pct_of_peak"],
+        "gbps_dispatch": s["gbps_dispatch"], "gbps_combine": s["gbps_combine"],
+        "bytes": {"dispatch": s["bytes_dispatch"], "combine": s["bytes_combine"], "rows": s["rows"]},
+        "copy_GBps_measured": copy_gbps,
+        "wall_s_timed_region": round(r["wall_s"], 4),
+        "roofline": {"kernel": "k_combine", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic, "us_avg": round(comb_avg_us, 2)},
+        "other": others,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -159,7 +159,8 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(int32_t* __restrict__ til
         }
     }
     __syncthreads();
-    if (group_offsets != nullptr && tid <= groups) group_offsets[tid] = s_off[tid * (E / groups)];
+    if (group_offsets != nullptr)
+        for (int g = tid; g <= groups; g += kScanThreads) group_offsets[g] = s_off[g * (E / groups)];
     const int64_t n = tiles * E;
     for (int64_t i = tid; i < n; i += kScanThreads) tile_counts[i] += s_off[i % E];
 }
