@@ -62,7 +62,9 @@ int64_t moe_dispatch_max_rows(int64_t T, int E, int k, int row_align) {
 
 size_t moe_dispatch_workspace_bytes(int64_t T, int E, int k, int groups) {
     if (max_rows_of(T, E, k, 1) < 0 || groups < 1 || E % groups != 0) return 0;
-    return (size_t)moe::dispatch_tiles(T) * (size_t)E * sizeof(int32_t);
+    size_t total = 0;
+    moe::dispatch_workspace_layout(T, E, k, &total);
+    return total;
 }
 
 int moe_dispatch(const void* x, const int32_t* topk_idx, int64_t T, int H, int E, int k,
@@ -111,6 +113,9 @@ int moe_dispatch(const void* x, const int32_t* topk_idx, int64_t T, int H, int E
     a.row_src = row_src;
     a.dst_row = dst_row;
     a.tile_counts = static_cast<int32_t*>(workspace);
+    size_t ws_total = 0;
+    const size_t rank_off = moe::dispatch_workspace_layout(T, E, k, &ws_total);
+    a.tile_rank = reinterpret_cast<int32_t*>(static_cast<unsigned char*>(workspace) + rank_off);
     a.max_rows = max_rows;
     moe::LaunchInfo info[3];
     const hipError_t e = moe::launch_dispatch(a, static_cast<hipStream_t>(stream), info);

@@ -18,16 +18,17 @@
 //                   counter). A token's rank within the tile for expert e is
 //                   the popcount of the lower lanes' bits plus the counts of
 //                   the earlier waves. Writes the tile's counts [tile, E] and
-//                   each slot's in-tile rank (into dst_row).
+//                   each slot's in-tile rank [T, k] (both in the workspace).
 //   K3 k_scan       one block. Per expert, an exclusive scan over tiles turns
 //                   tile counts into each tile's first row inside the segment
 //                   (this is what makes the order stable); totals are padded
 //                   to row_align and scanned over experts into offsets; group
 //                   offsets are read off the expert offsets.
-//   K4 k_scatter    blocks of TPB tokens: finalise dst_row / row_src, then
-//                   read each x row once with 16-byte loads and store it to
-//                   its k rows (FP8: one quantisation per token, k stores).
-//                   Extra leading blocks zero the pad rows.
+//   K4 k_scatter    one wave per (token, row chunk): rows = segment offset +
+//                   tile base + in-tile rank; reads each x row once with
+//                   16-byte streaming loads and stores it to its k rows (FP8:
+//                   one quantisation per token, k stores); the chunk-0 wave
+//                   publishes dst_row / row_src. Leading blocks zero pad rows.
 #include "moe_device.h"
 #include "launch.h"
 
@@ -36,6 +37,13 @@ namespace moe {
 constexpr int kHistWaves = kTileTokens / kWave;   // 4
 
 int64_t dispatch_tiles(int64_t T) { return (T + kTileTokens - 1) / kTileTokens; }
+
+size_t dispatch_workspace_layout(int64_t T, int E, int k, size_t* total) {
+    const size_t counts = (size_t)dispatch_tiles(T) * (size_t)E * sizeof(int32_t);
+    const size_t rank_off = (counts + 255) / 256 * 256;
+    *total = rank_off + (size_t)T * (size_t)k * sizeof(int32_t);
+    return rank_off;
+}
 
 // ---------------------------------------------------------------- K2
 
@@ -200,93 +208,105 @@ __device__ void zero_pad_rows(int pb, int pad_blocks_per_expert, int pad_rows_pe
     for (int i = threadIdx.x; i < rows; i += kScatterThreads) row_src[r0 + i] = -1;
 }
 
+constexpr int kScatterWaves = kScatterThreads / kWave;
+
+// One wave per (token, chunk of 64 lane units). A lane unit is 8 bf16 (16
+// bytes) for bf16 rows, or 16 bf16 in / 16 E4M3 codes out for FP8 rows, where
+// each aligned group of 8 lanes holds one 1x128 block. The token index is
+// wave-uniform, so its expert ids, in-tile ranks and tile bases come in
+// through scalar loads; the x row is read once through a range descriptor
+// (lanes past the row read zeros) and stored to each of the token's rows.
 template <bool FP8>
 __global__ __launch_bounds__(kScatterThreads) void k_scatter(
-    const uint16_t* __restrict__ x, const int32_t* __restrict__ topk_idx, int64_t T, int H, int E,
-    int k, int64_t max_rows, int tokens_per_block, int pad_blocks, int pad_blocks_per_expert,
-    int pad_rows_per_block, const int32_t* __restrict__ tile_base,
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ topk_idx,
+    const int32_t* __restrict__ tile_rank, const int32_t* __restrict__ tile_base,
     const int32_t* __restrict__ expert_counts, const int32_t* __restrict__ expert_offsets,
-    unsigned char* __restrict__ out, float* __restrict__ scales, int32_t* __restrict__ row_src,
-    int32_t* __restrict__ dst_row) {
-    extern __shared__ int32_t s_rows[];   // [tokens_per_block * k]
-
+    int64_t T, int H, int E, int k, int64_t max_rows, int pad_blocks,
+    int pad_blocks_per_expert, int pad_rows_per_block, unsigned char* __restrict__ out,
+    float* __restrict__ scales, int32_t* __restrict__ row_src, int32_t* __restrict__ dst_row) {
     if ((int)blockIdx.x < pad_blocks) {
         zero_pad_rows(blockIdx.x, pad_blocks_per_expert, pad_rows_per_block, H, FP8,
                       expert_counts, expert_offsets, out, scales, row_src);
         return;
     }
-    const int tid = threadIdx.x;
-    const int64_t t0 = (int64_t)(blockIdx.x - pad_blocks) * tokens_per_block;
-    const int nt = (int)min((int64_t)tokens_per_block, T - t0);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int U = FP8 ? H / 16 : H / 8;            // lane units per row
+    const int CW = (U + kWave - 1) / kWave;        // waves per token
+    const int64_t gw = (int64_t)(blockIdx.x - pad_blocks) * kScatterWaves +
+                       __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t t = gw / CW;
+    if (t >= T) return;
+    const int chunk = (int)(gw - t * CW);
+    const int u = chunk * kWave + lane;
+    const bool active = u < U;
 
-    // final rows: segment offset + tile's first row in the segment + in-tile rank
-    for (int i = tid; i < nt * k; i += kScatterThreads) {
-        const int64_t p = t0 * k + i;
-        const int64_t t = t0 + i / k;
-        const int e = topk_idx[p];
-        int r = -1;
-        if ((unsigned)e < (unsigned)E) {
-            r = tile_base[(t / kTileTokens) * E + e] + dst_row[p];
-            if (r < 0 || r >= max_rows) r = -1;   // never write outside the buffers
-            else row_src[r] = (int32_t)p;
-        }
-        dst_row[p] = r;
-        s_rows[i] = r;
-    }
-    __syncthreads();
-
-    if (!FP8) {
-        // 16-byte units of 8 bf16; each unit of x is loaded once, stored k times
-        const int C = H / 8;
-        const int64_t row_bytes = 2 * (int64_t)H;
-        const unsigned char* xb = reinterpret_cast<const unsigned char*>(x);
-        for (int u = tid; u < nt * C; u += kScatterThreads) {
-            const int tl = u / C;
-            const int c = u - tl * C;
-            const uint4 v = *reinterpret_cast<const uint4*>(xb + (t0 + tl) * row_bytes + 16 * (int64_t)c);
-            const int32_t* rows = s_rows + tl * k;
-            for (int j = 0; j < k; j++) {
-                const int r = rows[j];
-                if (r >= 0) *reinterpret_cast<uint4*>(out + (int64_t)r * row_bytes + 16 * (int64_t)c) = v;
-            }
-        }
+    // the token's activations: issued first so the row bookkeeping below
+    // overlaps the load latency
+    const auto xr = range_rsrc(x + t * (int64_t)H, 2 * H);
+    uint4 a, b;
+    if (FP8) {
+        a = load16_nt(xr, 32 * u);
+        b = load16_nt(xr, 32 * u + 16);
     } else {
-        // 16 elements per lane (32 bytes in, 16 bytes of codes out); the 8
-        // lanes of an aligned group hold one 1x128 block. C is a multiple of
-        // 8, so every group is entirely inside or outside the loop bound.
-        const int C = H / 16;
-        const int nb = H / 128;
-        const int64_t in_row_bytes = 2 * (int64_t)H;
-        const unsigned char* xb = reinterpret_cast<const unsigned char*>(x);
-        for (int u = tid; u < nt * C; u += kScatterThreads) {
-            const int tl = u / C;
-            const int c = u - tl * C;
-            const uint4* src = reinterpret_cast<const uint4*>(xb + (t0 + tl) * in_row_bytes + 32 * (int64_t)c);
-            const uint4 a = src[0];
-            const uint4 b = src[1];
-            float f[16];
-            unpack8(a, f);
-            unpack8(b, f + 8);
-            float amax = 0.0f;
+        a = load16_nt(xr, 16 * u);
+    }
+
+    uint4 q = make_uint4(0u, 0u, 0u, 0u);
+    float s = 0.0f;
+    if (FP8) {
+        float f[16];
+        unpack8(a, f);
+        unpack8(b, f + 8);
+        float amax = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 16; i++) amax = fmaxf(amax, fabsf(f[i]));
-            amax = group8_max(amax);
-            const float s = amax / 448.0f;
-            uint4 q = make_uint4(0u, 0u, 0u, 0u);
-            if (amax != 0.0f) {
-                q.x = f32x4_to_e4m3(f[0] / s, f[1] / s, f[2] / s, f[3] / s);
-                q.y = f32x4_to_e4m3(f[4] / s, f[5] / s, f[6] / s, f[7] / s);
-                q.z = f32x4_to_e4m3(f[8] / s, f[9] / s, f[10] / s, f[11] / s);
-                q.w = f32x4_to_e4m3(f[12] / s, f[13] / s, f[14] / s, f[15] / s);
+        for (int i = 0; i < 16; i++) amax = fmaxf(amax, fabsf(f[i]));
+        amax = group8_max(amax);
+        s = amax / 448.0f;
+        if (amax != 0.0f) {
+            q.x = f32x4_to_e4m3(f[0] / s, f[1] / s, f[2] / s, f[3] / s);
+            q.y = f32x4_to_e4m3(f[4] / s, f[5] / s, f[6] / s, f[7] / s);
+            q.z = f32x4_to_e4m3(f[8] / s, f[9] / s, f[10] / s, f[11] / s);
+            q.w = f32x4_to_e4m3(f[12] / s, f[13] / s, f[14] / s, f[15] / s);
+        }
+    }
+    const int nb = H / 128;
+    const bool scale_lane = FP8 && (u & 7) == 0;
+
+    const int64_t p0 = t * k;
+    const int32_t* tb = tile_base + (t / kTileTokens) * E;
+    for (int j0 = 0; j0 < k; j0 += 8) {
+        // destination rows of slots j0 .. j0+7: segment offset + tile's
+        // first row in the segment (tile_base) + in-tile rank
+        int r[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; jj++) {
+            r[jj] = -1;
+            if (j0 + jj < k) {
+                const int e = topk_idx[p0 + j0 + jj];
+                if ((unsigned)e < (unsigned)E) {
+                    const int rr = tb[e] + tile_rank[p0 + j0 + jj];
+                    r[jj] = (rr < 0 || rr >= max_rows) ? -1 : rr;   // never write outside
+                }
             }
-            const bool scale_lane = (c & 7) == 0;
-            const int blk = c >> 3;
-            const int32_t* rows = s_rows + tl * k;
-            for (int j = 0; j < k; j++) {
-                const int r = rows[j];
-                if (r >= 0) {
-                    *reinterpret_cast<uint4*>(out + (int64_t)r * H + 16 * (int64_t)c) = q;
-                    if (scale_lane) scales[(int64_t)r * nb + blk] = s;
+        }
+        if (chunk == 0) {
+            int mine = -1;
+#pragma unroll
+            for (int jj = 0; jj < 8; jj++) mine = (lane == jj) ? r[jj] : mine;
+            if (lane < 8 && j0 + lane < k) {
+                dst_row[p0 + j0 + lane] = mine;
+                if (mine >= 0) row_src[mine] = (int32_t)(p0 + j0 + lane);
+            }
+        }
+        if (active) {
+#pragma unroll
+            for (int jj = 0; jj < 8; jj++) {
+                if (r[jj] < 0) continue;
+                if (FP8) {
+                    *reinterpret_cast<uint4*>(out + (int64_t)r[jj] * H + 16 * (int64_t)u) = q;
+                    if (scale_lane) scales[(int64_t)r[jj] * nb + (u >> 3)] = s;
+                } else {
+                    *reinterpret_cast<uint4*>(out + (int64_t)r[jj] * 2 * H + 16 * (int64_t)u) = a;
                 }
             }
         }
@@ -304,7 +324,7 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream, LaunchInfo
     if (info) info[0] = LaunchInfo{tiles, kTileTokens, hist_lds, 0};
     if (tiles > 0) {
         k_tile_hist<<<dim3((unsigned)tiles), dim3(kTileTokens), hist_lds, stream>>>(
-            a.topk_idx, a.T, a.E, a.k, a.tile_counts, a.dst_row);
+            a.topk_idx, a.T, a.E, a.k, a.tile_counts, a.tile_rank);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
 
@@ -314,15 +334,10 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream, LaunchInfo
                                             a.expert_counts, a.expert_offsets, a.group_offsets);
     if ((err = hipGetLastError()) != hipSuccess) return err;
 
-    // K4: tokens per block so a block holds about 2048 16-byte units, fewer
-    // when T is small so that the grid still spreads over the chip
+    // K4: leading blocks zero pad rows, then one wave per (token, chunk)
     const int units = a.fp8 ? a.H / 16 : a.H / 8;
-    int64_t tpb = 2048 / units;
-    if (tpb < 1) tpb = 1;
-    const int64_t spread = (a.T + 1023) / 1024;
-    if (tpb > spread) tpb = spread < 1 ? 1 : spread;
-    while (tpb > 1 && tpb * a.k > 4096) tpb--;
-    const int64_t token_blocks = (a.T + tpb - 1) / tpb;
+    const int64_t waves_per_token = (units + kWave - 1) / kWave;
+    const int64_t token_blocks = (a.T * waves_per_token + kScatterWaves - 1) / kScatterWaves;
     int pad_per_expert = 0, pad_rows_per_block = 0;
     if (a.row_align > 1 && a.T > 0) {
         pad_per_expert = a.row_align - 1 < 4 ? a.row_align - 1 : 4;
@@ -330,20 +345,19 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream, LaunchInfo
     }
     const int64_t pad_blocks = (int64_t)a.E * pad_per_expert;
     const int64_t blocks = pad_blocks + token_blocks;
-    const size_t lds = (size_t)tpb * a.k * sizeof(int32_t);
-    if (info) info[2] = LaunchInfo{blocks, kScatterThreads, lds, tpb};
+    if (info) info[2] = LaunchInfo{blocks, kScatterThreads, 0, waves_per_token};
     if (blocks == 0) return hipSuccess;
     unsigned char* out = static_cast<unsigned char*>(a.out);
     const uint16_t* x = static_cast<const uint16_t*>(a.x);
     if (a.fp8)
-        k_scatter<true><<<dim3((unsigned)blocks), dim3(kScatterThreads), lds, stream>>>(
-            x, a.topk_idx, a.T, a.H, a.E, a.k, a.max_rows, (int)tpb, (int)pad_blocks, pad_per_expert,
-            pad_rows_per_block, a.tile_counts, a.expert_counts, a.expert_offsets, out,
+        k_scatter<true><<<dim3((unsigned)blocks), dim3(kScatterThreads), 0, stream>>>(
+            x, a.topk_idx, a.tile_rank, a.tile_counts, a.expert_counts, a.expert_offsets, a.T,
+            a.H, a.E, a.k, a.max_rows, (int)pad_blocks, pad_per_expert, pad_rows_per_block, out,
             a.out_scales, a.row_src, a.dst_row);
     else
-        k_scatter<false><<<dim3((unsigned)blocks), dim3(kScatterThreads), lds, stream>>>(
-            x, a.topk_idx, a.T, a.H, a.E, a.k, a.max_rows, (int)tpb, (int)pad_blocks, pad_per_expert,
-            pad_rows_per_block, a.tile_counts, a.expert_counts, a.expert_offsets, out,
+        k_scatter<false><<<dim3((unsigned)blocks), dim3(kScatterThreads), 0, stream>>>(
+            x, a.topk_idx, a.tile_rank, a.tile_counts, a.expert_counts, a.expert_offsets, a.T,
+            a.H, a.E, a.k, a.max_rows, (int)pad_blocks, pad_per_expert, pad_rows_per_block, out,
             a.out_scales, a.row_src, a.dst_row);
     return hipGetLastError();
 }

@@ -36,10 +36,15 @@ struct DispatchArgs {
     int32_t* row_src;
     int32_t* dst_row;
     int32_t* tile_counts;   // workspace [tiles, E]
+    int32_t* tile_rank;     // workspace [T, k]
     int64_t max_rows;       // rows in out / out_scales / row_src
 };
 
 int64_t dispatch_tiles(int64_t T);
+
+// Workspace layout: tile counts [tiles, E], then (256-byte aligned) in-tile
+// ranks [T, k]. Returns the byte offset of the ranks; *total gets the size.
+size_t dispatch_workspace_layout(int64_t T, int E, int k, size_t* total);
 
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream, LaunchInfo info[3]);
 

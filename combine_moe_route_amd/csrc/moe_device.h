@@ -98,14 +98,27 @@ __device__ __forceinline__ float shfl_xor_f32(float v, int mask) {
 
 // Buffer-descriptor word 3 for raw (untyped, stride 0) buffers on gfx9 parts.
 constexpr int kRawBufferConfig = 0x00020000;
+// Cache-policy bits of a buffer access: nt marks the data as streaming.
+constexpr int kCachePolicyNT = 2;
 
-// 16-byte load at byte `offset` of a wave-uniform range [base, base+bytes).
-// Offsets past `bytes` (including bytes == 0) read zeros instead of memory.
-__device__ __forceinline__ uint4 load_row16(const void* base, int bytes, int offset) {
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kRawBufferConfig);
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, offset, 0, 0);
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Descriptor for a wave-uniform byte range [base, base + bytes). Accesses at
+// offsets past `bytes` (all of them when bytes == 0) read zeros and drop
+// writes instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kRawBufferConfig);
+}
+
+// 16-byte streaming load at byte `offset` of a range descriptor.
+__device__ __forceinline__ uint4 load16_nt(__amdgpu_buffer_rsrc_t rs, int offset) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, offset, 0, kCachePolicyNT);
     return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// 16-byte streaming store (global address).
+__device__ __forceinline__ void store16_nt(void* p, const uint4& v) {
+    __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(p));
 }
 
 // ------------------------------------------------------------------ top-k keys

@@ -9,87 +9,172 @@
 // for any m: the full-E denominator cancels and is never formed.
 //
 // Layout: a group of S lanes (S = next power of two >= E, at most 64) owns one
-// token; lane g of the group holds experts g, g+S, g+2S, ... (NV per lane),
-// so the logit row is read with coalesced loads. Each of the k rounds takes
-// the group maximum of a packed (order key, ~expert) word with xor shuffles,
-// and the lane owning the winner clears it. Round r's winner is kept by lane
-// r % S in register slot r / S, which then writes slot r of the output.
+// token; lane g of the group holds experts g, g+S, g+2S, ... (NV per lane), so
+// the logit row is read with coalesced loads. Each of the k rounds:
+//   1. every lane takes the best of its remaining candidates (strict >, so
+//      equal logits keep the lower expert),
+//   2. the group maximum of the lanes' order keys (uint32 whose order is the
+//      numeric order, -0 taken as +0) comes from a butterfly over DPP row
+//      permutes and the gfx950 permlane16/permlane32 swaps (registers only),
+//   3. a ballot of the lanes holding that maximum names the winner; if several
+//      lanes tie, a second butterfly takes the smallest expert index,
+//   4. the winning lane retires that candidate.
+// Round r's winner is kept by lane r % S in register slot r / S, which then
+// writes slot r of the output.
 #include "moe_device.h"
 #include "launch.h"
 
 namespace moe {
 
-template <int NV>
-__global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ logits,
-                                                    int64_t T, int E, int k, int S,
-                                                    int32_t* __restrict__ topk_idx,
+namespace {
+
+constexpr int kDppRowMirror = 0x140;   // lane i <-> 15-i within each row of 16
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Butterfly over aligned groups of S lanes; OP(a, b) must be commutative and
+// associative. Every lane of a group ends with the group's result.
+template <int S, typename F>
+__device__ __forceinline__ uint32_t group_reduce(uint32_t v, F op) {
+    if (S > 1) v = op(v, dpp_u32<kDppQuadXor1>(v));
+    if (S > 2) v = op(v, dpp_u32<kDppQuadXor2>(v));
+    if (S > 4) v = op(v, dpp_u32<kDppRowHalfMirror>(v));
+    if (S > 8) v = op(v, dpp_u32<kDppRowMirror>(v));
+    if (S > 16) {
+        const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        v = op(p[0], p[1]);
+    }
+    if (S > 32) {
+        const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        v = op(p[0], p[1]);
+    }
+    return v;
+}
+
+struct UMax {
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; }
+};
+struct UMin {
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? a : b; }
+};
+struct FAdd {
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const {
+        return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+    }
+};
+
+}  // namespace
+
+template <int S, int NV>
+__global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ logits, int64_t T,
+                                                    int E, int k, int32_t* __restrict__ topk_idx,
                                                     float* __restrict__ topk_w) {
+    constexpr uint32_t kNone = 0xFFFFFFFFu;
     const int lane = threadIdx.x & (kWave - 1);
     const int g = lane & (S - 1);
-    const int tokens_per_wave = kWave / S;
+    const int base = lane & ~(S - 1);          // first lane of this group
+    constexpr int kTokensPerWave = kWave / S;
     const int64_t wave = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
-    const int64_t t = wave * tokens_per_wave + lane / S;
+    const int64_t t = wave * kTokensPerWave + lane / S;
     const bool live = t < T;
 
-    uint64_t cand[NV];
+    // candidates as order keys (unsigned order == numeric order, -0 == +0);
+    // 0 marks an empty slot, real keys are never 0
+    uint32_t c[NV];
     const float* row = logits + (live ? t : 0) * (int64_t)E;
 #pragma unroll
     for (int i = 0; i < NV; i++) {
         const int e = g + S * i;
-        cand[i] = (live && e < E) ? topk_pack(row[e], e) : 0ull;
+        c[i] = (live && e < E) ? order_key(row[e]) : 0u;
     }
 
-    uint64_t sel[NV];
+    uint32_t sel_key[NV];
+    int sel_e[NV];
 #pragma unroll
-    for (int i = 0; i < NV; i++) sel[i] = 0ull;
-    uint64_t first = 0ull;
+    for (int i = 0; i < NV; i++) {
+        sel_key[i] = 0u;
+        sel_e[i] = 0;
+    }
+    uint32_t first = 0u;
 
     for (int r = 0; r < k; r++) {
-        uint64_t best = cand[0];
+        // best remaining candidate of this lane (strict >: ties keep the lower slot)
+        uint32_t best = c[0];
+        int bslot = 0;
 #pragma unroll
-        for (int i = 1; i < NV; i++) best = cand[i] > best ? cand[i] : best;
-        for (int m = S >> 1; m > 0; m >>= 1) {
-            const uint64_t o = shfl_xor_u64(best, m);
-            best = o > best ? o : best;
+        for (int i = 1; i < NV; i++)
+            if (c[i] > best) {
+                best = c[i];
+                bslot = i;
+            }
+        const uint32_t bidx = best == 0u ? kNone : (uint32_t)(g + S * bslot);
+        // group maximum, then who holds it
+        const uint32_t m = group_reduce<S>(best, UMax());
+        const bool holds = best == m && best != 0u;
+        const uint64_t mask = __ballot(holds);
+        const uint64_t gmask = (S == kWave) ? mask : (mask >> base) & ((1ull << S) - 1ull);
+        uint32_t we;
+        if (NV == 1) {
+            // one candidate per lane: the lowest holding lane is the lowest expert
+            we = gmask ? (uint32_t)__builtin_ctzll(gmask) : 0u;
+        } else if (__popcll(gmask) <= 1) {
+            // S == 64 here, so the holder is wave-uniform
+            const int wl = gmask ? (int)__builtin_ctzll(gmask) : 0;
+            we = (uint32_t)__builtin_amdgcn_readlane((int)bidx, wl);
+        } else {
+            we = group_reduce<S>(holds ? bidx : kNone, UMin());
         }
-        if (r == 0) first = best;
-        const int we = topk_expert(best);
-        if ((we & (S - 1)) == g) {
-            const int slot = we / S;
+        if (r == 0) first = m;
+        // retire the winner
+        if ((int)(we & (S - 1)) == g) {
+            const int slot = (int)(we / S);
 #pragma unroll
             for (int i = 0; i < NV; i++)
-                if (i == slot) cand[i] = 0ull;
+                if (i == slot) c[i] = 0u;
         }
+        // record round r
         if ((r & (S - 1)) == g) {
             const int slot = r / S;
 #pragma unroll
             for (int i = 0; i < NV; i++)
-                if (i == slot) sel[i] = best;
+                if (i == slot) {
+                    sel_key[i] = m;
+                    sel_e[i] = (int)we;
+                }
         }
     }
 
     // weights: exp(l_j - l_max) / sum over the chosen, fp32, true division
-    const float m = topk_value(first);
     float ex[NV];
     float part = 0.0f;
 #pragma unroll
     for (int i = 0; i < NV; i++) {
         const int r = g + S * i;
-        ex[i] = (r < k) ? expf(topk_value(sel[i]) - m) : 0.0f;
+        ex[i] = (r < k) ? expf(key_value(sel_key[i]) - key_value(first)) : 0.0f;
         part += ex[i];
     }
-    for (int msk = S >> 1; msk > 0; msk >>= 1) part += shfl_xor_f32(part, msk);
+    const float sum = __uint_as_float(group_reduce<S>(__float_as_uint(part), FAdd()));
 
     if (live) {
 #pragma unroll
         for (int i = 0; i < NV; i++) {
             const int r = g + S * i;
             if (r < k) {
-                topk_idx[t * k + r] = topk_expert(sel[i]);
-                topk_w[t * k + r] = ex[i] / part;
+                topk_idx[t * k + r] = sel_e[i];
+                topk_w[t * k + r] = ex[i] / sum;
             }
         }
     }
+}
+
+template <int S, int NV>
+static void launch_s(const float* logits, int64_t T, int E, int k, int32_t* topk_idx,
+                     float* topk_w, hipStream_t stream, int64_t blocks) {
+    k_route_topk<S, NV><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(logits, T, E, k, topk_idx,
+                                                                        topk_w);
 }
 
 hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k,
@@ -101,24 +186,22 @@ hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k,
     const int threads = 256;
     const int64_t tokens_per_block = (threads / kWave) * (kWave / S);
     const int64_t blocks = (T + tokens_per_block - 1) / tokens_per_block;
-    if (info) {
-        info->grid = blocks;
-        info->block = threads;
-        info->lds = 0;
-        info->param = S;
-    }
+    if (info) *info = LaunchInfo{blocks, threads, 0, S};
     if (blocks == 0) return hipSuccess;
-    const dim3 grid((unsigned)blocks), block(threads);
-    if (nv <= 1)
-        k_route_topk<1><<<grid, block, 0, stream>>>(logits, T, E, k, S, topk_idx, topk_w);
-    else if (nv <= 2)
-        k_route_topk<2><<<grid, block, 0, stream>>>(logits, T, E, k, S, topk_idx, topk_w);
-    else if (nv <= 4)
-        k_route_topk<4><<<grid, block, 0, stream>>>(logits, T, E, k, S, topk_idx, topk_w);
-    else if (nv <= 8)
-        k_route_topk<8><<<grid, block, 0, stream>>>(logits, T, E, k, S, topk_idx, topk_w);
-    else
-        k_route_topk<16><<<grid, block, 0, stream>>>(logits, T, E, k, S, topk_idx, topk_w);
+    switch (S) {
+        case 1: launch_s<1, 1>(logits, T, E, k, topk_idx, topk_w, stream, blocks); break;
+        case 2: launch_s<2, 1>(logits, T, E, k, topk_idx, topk_w, stream, blocks); break;
+        case 4: launch_s<4, 1>(logits, T, E, k, topk_idx, topk_w, stream, blocks); break;
+        case 8: launch_s<8, 1>(logits, T, E, k, topk_idx, topk_w, stream, blocks); break;
+        case 16: launch_s<16, 1>(logits, T, E, k, topk_idx, topk_w, stream, blocks); break;
+        case 32: launch_s<32, 1>(logits, T, E, k, topk_idx, topk_w, stream, blocks); break;
+        default:
+            if (nv <= 1) launch_s<64, 1>(logits, T, E, k, topk_idx, topk_w, stream, blocks);
+            else if (nv <= 2) launch_s<64, 2>(logits, T, E, k, topk_idx, topk_w, stream, blocks);
+            else if (nv <= 4) launch_s<64, 4>(logits, T, E, k, topk_idx, topk_w, stream, blocks);
+            else if (nv <= 8) launch_s<64, 8>(logits, T, E, k, topk_idx, topk_w, stream, blocks);
+            else launch_s<64, 16>(logits, T, E, k, topk_idx, topk_w, stream, blocks);
+    }
     return hipGetLastError();
 }
 

@@ -57,8 +57,9 @@ def test_max_rows_and_workspace():
     assert lib.moe_dispatch_max_rows(10, 4, 2, 0) == -1          # row_align < 1
     assert lib.moe_dispatch_max_rows(10, 4, 2, 1025) == -1
     assert lib.moe_dispatch_max_rows(2 ** 28, 8, 8, 1) == -1     # rows overflow int32
-    assert lib.moe_dispatch_workspace_bytes(16384, 256, 8, 32) == 64 * 256 * 4
-    assert lib.moe_dispatch_workspace_bytes(300, 8, 2, 1) == 2 * 8 * 4
+    # tile counts [tiles, E], then (256-byte aligned) in-tile ranks [T, k]
+    assert lib.moe_dispatch_workspace_bytes(16384, 256, 8, 32) == 64 * 256 * 4 + 16384 * 8 * 4
+    assert lib.moe_dispatch_workspace_bytes(300, 8, 2, 1) == 256 + 300 * 2 * 4
     assert lib.moe_dispatch_workspace_bytes(0, 8, 2, 1) == 0
     assert lib.moe_dispatch_workspace_bytes(300, 8, 2, 3) == 0   # E % groups != 0
 

@@ -240,3 +240,17 @@ def test_fp8_quantiser_exhaustive_domain(dev):
             done += n
             chunk = [rest] if len(rest) else []
             log(f"  exhaustive: amax up to {a:#06x}, {done} blocks")
+
+
+@pytest.mark.parametrize("E", [1, 2, 3, 4, 5, 7, 8, 9, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128,
+                               129, 200, 256, 257, 384, 511, 512, 513, 777, 1000, 1024])
+def test_router_every_group_width(dev, E):
+    """Every lane-group width (1..64 lanes per token) and candidates per lane
+    (1..16), with k from 1 to E, against the oracle."""
+    T = 333
+    ks = sorted({1, min(E, 2), min(E, 3), min(E, 8), min(E, 16)} | ({E} if E <= 64 else set()))
+    l = gen_logits(T, E, seed=E)
+    lt = np.round(l * 2) / 2                              # many ties
+    for k in ks:
+        route_parity(l, k, dev)
+        route_parity(lt.astype(np.float32), k, dev)
