@@ -23,7 +23,8 @@
 //                   tile counts into each tile's first row inside the segment
 //                   (this is what makes the order stable); totals are padded
 //                   to row_align and scanned over experts into offsets; group
-//                   offsets are read off the expert offsets.
+//                   offsets are read off the expert offsets. Several threads
+//                   share an expert, each scanning a contiguous tile range.
 //   K4 k_scatter    one wave per (token, row chunk): rows = segment offset +
 //                   tile base + in-tile rank; reads each x row once with
 //                   16-byte streaming loads and stores it to its k rows (FP8:
@@ -64,11 +65,17 @@ __global__ __launch_bounds__(kTileTokens) void k_tile_hist(const int32_t* __rest
     for (int i = tid; i < kHistWaves * E; i += kTileTokens) mask[i] = 0ull;
     __syncthreads();
 
+    // expert ids are loaded in batches of 8 before any LDS atomic, so the
+    // loads are in flight together
     const uint64_t bit = 1ull << lane;
     if (live) {
-        for (int j = 0; j < k; j++) {
-            const int e = topk_idx[t * k + j];
-            if ((unsigned)e < (unsigned)E) atomicOr(&mask[w * E + e], bit);
+        for (int j0 = 0; j0 < k; j0 += 8) {
+            int e[8];
+#pragma unroll
+            for (int jj = 0; jj < 8; jj++) e[jj] = (j0 + jj < k) ? topk_idx[t * k + j0 + jj] : -1;
+#pragma unroll
+            for (int jj = 0; jj < 8; jj++)
+                if ((unsigned)e[jj] < (unsigned)E) atomicOr(&mask[w * E + e[jj]], bit);
         }
     }
     __syncthreads();
@@ -86,11 +93,18 @@ __global__ __launch_bounds__(kTileTokens) void k_tile_hist(const int32_t* __rest
 
     if (live) {
         const uint64_t lower = bit - 1ull;
-        for (int j = 0; j < k; j++) {
-            const int e = topk_idx[t * k + j];
-            int r = -1;
-            if ((unsigned)e < (unsigned)E) r = before[w * E + e] + __popcll(mask[w * E + e] & lower);
-            tile_rank[t * k + j] = r;
+        for (int j0 = 0; j0 < k; j0 += 8) {
+            int e[8];
+#pragma unroll
+            for (int jj = 0; jj < 8; jj++) e[jj] = (j0 + jj < k) ? topk_idx[t * k + j0 + jj] : -1;
+#pragma unroll
+            for (int jj = 0; jj < 8; jj++) {
+                if (j0 + jj >= k) break;
+                int r = -1;
+                if ((unsigned)e[jj] < (unsigned)E)
+                    r = before[w * E + e[jj]] + __popcll(mask[w * E + e[jj]] & lower);
+                tile_rank[t * k + j0 + jj] = r;
+            }
         }
     }
 }
@@ -109,44 +123,58 @@ __device__ __forceinline__ int wave_inclusive_sum(int v) {
     return v;
 }
 
+// Threads are laid out as tid = p * Ep + e (Ep = E rounded up to a power of
+// two): P = 1024 / Ep threads share expert e, thread p owning a contiguous
+// range of tiles. Pass 1 sums each range with independent loads in batches of
+// 8; an LDS exchange gives each range its start inside the expert's segment;
+// the p == 0 threads scan the padded totals over experts; pass 2 rewrites the
+// tile counts as tile bases (segment offset + rows of earlier tiles).
 __global__ __launch_bounds__(kScanThreads) void k_scan(int32_t* __restrict__ tile_counts,
                                                        int64_t tiles, int E, int row_align,
                                                        int groups,
                                                        int32_t* __restrict__ expert_counts,
                                                        int32_t* __restrict__ expert_offsets,
                                                        int32_t* __restrict__ group_offsets) {
+    __shared__ int32_t s_part[kScanThreads];
     __shared__ int32_t s_off[1025];
     __shared__ int32_t s_wave[kScanThreads / kWave];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
-    const int e = tid;
+    int Ep = 1;
+    while (Ep < E) Ep <<= 1;
+    const int P = kScanThreads / Ep;
+    const int e = tid & (Ep - 1);
+    const int p = tid / Ep;
+    const bool real = e < E;
+    const int64_t per = (tiles + P - 1) / P;
+    const int64_t b0 = min(tiles, (int64_t)p * per);
+    const int64_t b1 = min(tiles, b0 + per);
 
-    // per expert: exclusive scan over tiles (in place), total count
-    int cnt = 0;
-    if (e < E) {
-        int64_t b = 0;
-        for (; b + 4 <= tiles; b += 4) {
-            const int c0 = tile_counts[(b + 0) * E + e];
-            const int c1 = tile_counts[(b + 1) * E + e];
-            const int c2 = tile_counts[(b + 2) * E + e];
-            const int c3 = tile_counts[(b + 3) * E + e];
-            tile_counts[(b + 0) * E + e] = cnt;
-            tile_counts[(b + 1) * E + e] = cnt + c0;
-            tile_counts[(b + 2) * E + e] = cnt + c0 + c1;
-            tile_counts[(b + 3) * E + e] = cnt + c0 + c1 + c2;
-            cnt += c0 + c1 + c2 + c3;
-        }
-        for (; b < tiles; b++) {
-            const int c = tile_counts[b * E + e];
-            tile_counts[b * E + e] = cnt;
-            cnt += c;
+    // pass 1: rows of this expert in tiles [b0, b1)
+    int part = 0;
+    if (real) {
+        for (int64_t b = b0; b < b1; b += 8) {
+            int c[8];
+#pragma unroll
+            for (int i = 0; i < 8; i++) c[i] = (b + i < b1) ? tile_counts[(b + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < 8; i++) part += c[i];
         }
     }
-    const int padded = (e < E) ? (cnt + row_align - 1) / row_align * row_align : 0;
+    s_part[tid] = part;
+    __syncthreads();
+    int before = 0, cnt = 0;
+    for (int q = 0; q < P; q++) {
+        const int v = s_part[q * Ep + e];
+        before += q < p ? v : 0;
+        cnt += v;
+    }
+    const int padded = (p == 0 && real) ? (cnt + row_align - 1) / row_align * row_align : 0;
 
-    // block-wide exclusive scan of the padded counts over experts
+    // exclusive scan of the padded totals over experts (the p == 0 threads
+    // are tid 0 .. Ep-1, in expert order; all others add zero)
     const int incl = wave_inclusive_sum(padded);
     if (lane == kWave - 1) s_wave[wave] = incl;
     __syncthreads();
@@ -157,7 +185,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(int32_t* __restrict__ til
     }
     __syncthreads();
     const int excl = s_wave[wave] + incl - padded;
-    if (e < E) {
+    if (p == 0 && real) {
         expert_counts[e] = cnt;
         expert_offsets[e] = excl;
         s_off[e] = excl;
@@ -169,8 +197,22 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(int32_t* __restrict__ til
     __syncthreads();
     if (group_offsets != nullptr)
         for (int g = tid; g <= groups; g += kScanThreads) group_offsets[g] = s_off[g * (E / groups)];
-    const int64_t n = tiles * E;
-    for (int64_t i = tid; i < n; i += kScanThreads) tile_counts[i] += s_off[i % E];
+
+    // pass 2: tile bases
+    if (real) {
+        int run = s_off[e] + before;
+        for (int64_t b = b0; b < b1; b += 8) {
+            int c[8];
+#pragma unroll
+            for (int i = 0; i < 8; i++) c[i] = (b + i < b1) ? tile_counts[(b + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < 8; i++)
+                if (b + i < b1) {
+                    tile_counts[(b + i) * E + e] = run;
+                    run += c[i];
+                }
+        }
+    }
 }
 
 // ---------------------------------------------------------------- K4
@@ -196,41 +238,71 @@ __device__ void zero_pad_rows(int pb, int pad_blocks_per_expert, int pad_rows_pe
     const int units = (int)(row_bytes / 16);
     const int64_t r0 = (int64_t)first + lo;
     const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-    for (int u = threadIdx.x; u < rows * units; u += kScatterThreads) {
+    for (int u = threadIdx.x; u < rows * units; u += blockDim.x) {
         const int rr = u / units;
         const int c = u - rr * units;
         *reinterpret_cast<uint4*>(out + (r0 + rr) * row_bytes + 16 * (int64_t)c) = z;
     }
     if (fp8) {
         const int nb = H / 128;
-        for (int i = threadIdx.x; i < rows * nb; i += kScatterThreads) scales[r0 * nb + i] = 0.0f;
+        for (int i = threadIdx.x; i < rows * nb; i += blockDim.x) scales[r0 * nb + i] = 0.0f;
     }
-    for (int i = threadIdx.x; i < rows; i += kScatterThreads) row_src[r0 + i] = -1;
+    for (int i = threadIdx.x; i < rows; i += blockDim.x) row_src[r0 + i] = -1;
 }
 
 constexpr int kScatterWaves = kScatterThreads / kWave;
 
-// One wave per (token, chunk of 64 lane units). A lane unit is 8 bf16 (16
-// bytes) for bf16 rows, or 16 bf16 in / 16 E4M3 codes out for FP8 rows, where
-// each aligned group of 8 lanes holds one 1x128 block. The token index is
-// wave-uniform, so its expert ids, in-tile ranks and tile bases come in
-// through scalar loads; the x row is read once through a range descriptor
-// (lanes past the row read zeros) and stored to each of the token's rows.
-template <bool FP8>
-__global__ __launch_bounds__(kScatterThreads) void k_scatter(
+// Destination rows of slots j0 .. j0+7 of token t: segment offset + tile's
+// first row in the segment (tile_base) + in-tile rank; -1 for dropped slots.
+__device__ __forceinline__ void slot_rows(const int32_t* __restrict__ topk_idx,
+                                          const int32_t* __restrict__ tile_rank,
+                                          const int32_t* __restrict__ tb, int64_t p0, int j0,
+                                          int k, int E, int64_t max_rows, int r[8]) {
+#pragma unroll
+    for (int jj = 0; jj < 8; jj++) {
+        r[jj] = -1;
+        if (j0 + jj < k) {
+            const int e = topk_idx[p0 + j0 + jj];
+            if ((unsigned)e < (unsigned)E) {
+                const int rr = tb[e] + tile_rank[p0 + j0 + jj];
+                r[jj] = (rr < 0 || rr >= max_rows) ? -1 : rr;   // never write outside
+            }
+        }
+    }
+}
+
+// The wave that owns slots j0 .. j0+7 publishes dst_row and row_src for them.
+__device__ __forceinline__ void publish_rows(int lane, int64_t p0, int j0, int k, const int r[8],
+                                             int32_t* __restrict__ dst_row,
+                                             int32_t* __restrict__ row_src) {
+    int mine = -1;
+#pragma unroll
+    for (int jj = 0; jj < 8; jj++) mine = (lane == jj) ? r[jj] : mine;
+    if (lane < 8 && j0 + lane < k) {
+        dst_row[p0 + j0 + lane] = mine;
+        if (mine >= 0) row_src[mine] = (int32_t)(p0 + j0 + lane);
+    }
+}
+
+// bf16 rows. One wave per (token, chunk of 64 lane units of 8 bf16 = 16
+// bytes). The token index is wave-uniform, so its expert ids, in-tile ranks
+// and tile bases come in through scalar loads; the x row is read once through
+// a range descriptor (lanes past the row read zeros) and stored to each of the
+// token's rows.
+__global__ __launch_bounds__(kScatterThreads) void k_scatter_bf16(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ topk_idx,
     const int32_t* __restrict__ tile_rank, const int32_t* __restrict__ tile_base,
     const int32_t* __restrict__ expert_counts, const int32_t* __restrict__ expert_offsets,
     int64_t T, int H, int E, int k, int64_t max_rows, int pad_blocks,
     int pad_blocks_per_expert, int pad_rows_per_block, unsigned char* __restrict__ out,
-    float* __restrict__ scales, int32_t* __restrict__ row_src, int32_t* __restrict__ dst_row) {
+    int32_t* __restrict__ row_src, int32_t* __restrict__ dst_row) {
     if ((int)blockIdx.x < pad_blocks) {
-        zero_pad_rows(blockIdx.x, pad_blocks_per_expert, pad_rows_per_block, H, FP8,
-                      expert_counts, expert_offsets, out, scales, row_src);
+        zero_pad_rows(blockIdx.x, pad_blocks_per_expert, pad_rows_per_block, H, false,
+                      expert_counts, expert_offsets, out, nullptr, row_src);
         return;
     }
     const int lane = threadIdx.x & (kWave - 1);
-    const int U = FP8 ? H / 16 : H / 8;            // lane units per row
+    const int U = H / 8;                           // 16-byte units per row
     const int CW = (U + kWave - 1) / kWave;        // waves per token
     const int64_t gw = (int64_t)(blockIdx.x - pad_blocks) * kScatterWaves +
                        __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -238,22 +310,58 @@ __global__ __launch_bounds__(kScatterThreads) void k_scatter(
     if (t >= T) return;
     const int chunk = (int)(gw - t * CW);
     const int u = chunk * kWave + lane;
-    const bool active = u < U;
 
-    // the token's activations: issued first so the row bookkeeping below
-    // overlaps the load latency
-    const auto xr = range_rsrc(x + t * (int64_t)H, 2 * H);
-    uint4 a, b;
-    if (FP8) {
-        a = load16_nt(xr, 32 * u);
-        b = load16_nt(xr, 32 * u + 16);
-    } else {
-        a = load16_nt(xr, 16 * u);
+    const uint4 a = load16_nt(range_rsrc(x + t * (int64_t)H, 2 * H), 16 * u);
+    const int64_t p0 = t * k;
+    const int32_t* tb = tile_base + (t / kTileTokens) * E;
+    for (int j0 = 0; j0 < k; j0 += 8) {
+        int r[8];
+        slot_rows(topk_idx, tile_rank, tb, p0, j0, k, E, max_rows, r);
+        if (chunk == 0) publish_rows(lane, p0, j0, k, r, dst_row, row_src);
+        if (u < U) {
+#pragma unroll
+            for (int jj = 0; jj < 8; jj++)
+                if (r[jj] >= 0)
+                    *reinterpret_cast<uint4*>(out + (int64_t)r[jj] * 2 * H + 16 * (int64_t)u) = a;
+        }
     }
+}
 
-    uint4 q = make_uint4(0u, 0u, 0u, 0u);
-    float s = 0.0f;
-    if (FP8) {
+// FP8 rows. One block per token, W waves; wave w handles row chunks w, w+W,
+// ... of 64 lane units, a unit being 16 bf16 in (32 bytes) and 16 E4M3 codes
+// out (16 bytes), so each aligned group of 8 lanes holds one 1x128 block and
+// reduces its amax over DPP. The token is quantised once; its codes are stored
+// to each destination row, and its 1x128 scales are staged in LDS and written
+// to each row's scale segment with one contiguous store (instead of many small
+// pieces from different waves, which cost HBM read-modify-write cycles).
+__global__ __launch_bounds__(1024) void k_scatter_fp8(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ topk_idx,
+    const int32_t* __restrict__ tile_rank, const int32_t* __restrict__ tile_base,
+    const int32_t* __restrict__ expert_counts, const int32_t* __restrict__ expert_offsets,
+    int64_t T, int H, int E, int k, int64_t max_rows, int pad_blocks,
+    int pad_blocks_per_expert, int pad_rows_per_block, unsigned char* __restrict__ out,
+    float* __restrict__ scales, int32_t* __restrict__ row_src, int32_t* __restrict__ dst_row) {
+    extern __shared__ float s_scale[];             // [H / 128]
+    if ((int)blockIdx.x < pad_blocks) {
+        zero_pad_rows(blockIdx.x, pad_blocks_per_expert, pad_rows_per_block, H, true,
+                      expert_counts, expert_offsets, out, scales, row_src);
+        return;
+    }
+    const int64_t t = blockIdx.x - pad_blocks;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int W = blockDim.x / kWave;
+    const int U = H / 16;                          // lane units per row
+    const int CW = (U + kWave - 1) / kWave;
+    const int nb = H / 128;
+    const auto xr = range_rsrc(x + t * (int64_t)H, 2 * H);
+    const int64_t p0 = t * k;
+    const int32_t* tb = tile_base + (t / kTileTokens) * E;
+
+    for (int chunk = w; chunk < CW; chunk += W) {
+        const int u = chunk * kWave + lane;
+        const uint4 a = load16_nt(xr, 32 * u);
+        const uint4 b = load16_nt(xr, 32 * u + 16);
         float f[16];
         unpack8(a, f);
         unpack8(b, f + 8);
@@ -261,55 +369,35 @@ __global__ __launch_bounds__(kScatterThreads) void k_scatter(
 #pragma unroll
         for (int i = 0; i < 16; i++) amax = fmaxf(amax, fabsf(f[i]));
         amax = group8_max(amax);
-        s = amax / 448.0f;
+        const float s = amax / 448.0f;
+        uint4 q = make_uint4(0u, 0u, 0u, 0u);
         if (amax != 0.0f) {
             q.x = f32x4_to_e4m3(f[0] / s, f[1] / s, f[2] / s, f[3] / s);
             q.y = f32x4_to_e4m3(f[4] / s, f[5] / s, f[6] / s, f[7] / s);
             q.z = f32x4_to_e4m3(f[8] / s, f[9] / s, f[10] / s, f[11] / s);
             q.w = f32x4_to_e4m3(f[12] / s, f[13] / s, f[14] / s, f[15] / s);
         }
+        if (u < U && (u & 7) == 0) s_scale[u >> 3] = s;
+        for (int j0 = 0; j0 < k; j0 += 8) {
+            int r[8];
+            slot_rows(topk_idx, tile_rank, tb, p0, j0, k, E, max_rows, r);
+            if (chunk == 0) publish_rows(lane, p0, j0, k, r, dst_row, row_src);
+            if (u < U) {
+#pragma unroll
+                for (int jj = 0; jj < 8; jj++)
+                    if (r[jj] >= 0)
+                        *reinterpret_cast<uint4*>(out + (int64_t)r[jj] * H + 16 * (int64_t)u) = q;
+            }
+        }
     }
-    const int nb = H / 128;
-    const bool scale_lane = FP8 && (u & 7) == 0;
-
-    const int64_t p0 = t * k;
-    const int32_t* tb = tile_base + (t / kTileTokens) * E;
-    for (int j0 = 0; j0 < k; j0 += 8) {
-        // destination rows of slots j0 .. j0+7: segment offset + tile's
-        // first row in the segment (tile_base) + in-tile rank
-        int r[8];
-#pragma unroll
-        for (int jj = 0; jj < 8; jj++) {
-            r[jj] = -1;
-            if (j0 + jj < k) {
-                const int e = topk_idx[p0 + j0 + jj];
-                if ((unsigned)e < (unsigned)E) {
-                    const int rr = tb[e] + tile_rank[p0 + j0 + jj];
-                    r[jj] = (rr < 0 || rr >= max_rows) ? -1 : rr;   // never write outside
-                }
-            }
-        }
-        if (chunk == 0) {
-            int mine = -1;
-#pragma unroll
-            for (int jj = 0; jj < 8; jj++) mine = (lane == jj) ? r[jj] : mine;
-            if (lane < 8 && j0 + lane < k) {
-                dst_row[p0 + j0 + lane] = mine;
-                if (mine >= 0) row_src[mine] = (int32_t)(p0 + j0 + lane);
-            }
-        }
-        if (active) {
-#pragma unroll
-            for (int jj = 0; jj < 8; jj++) {
-                if (r[jj] < 0) continue;
-                if (FP8) {
-                    *reinterpret_cast<uint4*>(out + (int64_t)r[jj] * H + 16 * (int64_t)u) = q;
-                    if (scale_lane) scales[(int64_t)r[jj] * nb + (u >> 3)] = s;
-                } else {
-                    *reinterpret_cast<uint4*>(out + (int64_t)r[jj] * 2 * H + 16 * (int64_t)u) = a;
-                }
-            }
-        }
+    __syncthreads();
+    // scale segments: wave w writes the segments of slots w, w+W, ...
+    for (int j = w; j < k; j += W) {
+        const int e = topk_idx[p0 + j];
+        if ((unsigned)e >= (unsigned)E) continue;
+        const int rr = tb[e] + tile_rank[p0 + j];
+        if (rr < 0 || rr >= max_rows) continue;
+        for (int i = lane; i < nb; i += kWave) scales[(int64_t)rr * nb + i] = s_scale[i];
     }
 }
 
@@ -334,31 +422,41 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream, LaunchInfo
                                             a.expert_counts, a.expert_offsets, a.group_offsets);
     if ((err = hipGetLastError()) != hipSuccess) return err;
 
-    // K4: leading blocks zero pad rows, then one wave per (token, chunk)
-    const int units = a.fp8 ? a.H / 16 : a.H / 8;
-    const int64_t waves_per_token = (units + kWave - 1) / kWave;
-    const int64_t token_blocks = (a.T * waves_per_token + kScatterWaves - 1) / kScatterWaves;
+    // K4: leading blocks zero pad rows, then the token work
     int pad_per_expert = 0, pad_rows_per_block = 0;
     if (a.row_align > 1 && a.T > 0) {
         pad_per_expert = a.row_align - 1 < 4 ? a.row_align - 1 : 4;
         pad_rows_per_block = (a.row_align - 1 + pad_per_expert - 1) / pad_per_expert;
     }
     const int64_t pad_blocks = (int64_t)a.E * pad_per_expert;
-    const int64_t blocks = pad_blocks + token_blocks;
-    if (info) info[2] = LaunchInfo{blocks, kScatterThreads, 0, waves_per_token};
-    if (blocks == 0) return hipSuccess;
     unsigned char* out = static_cast<unsigned char*>(a.out);
     const uint16_t* x = static_cast<const uint16_t*>(a.x);
-    if (a.fp8)
-        k_scatter<true><<<dim3((unsigned)blocks), dim3(kScatterThreads), 0, stream>>>(
+    if (a.fp8) {
+        // one block per token, one wave per 64-unit chunk (at most 16 waves)
+        const int units = a.H / 16;
+        int waves = (units + kWave - 1) / kWave;
+        if (waves > 16) waves = 16;
+        const int64_t blocks = pad_blocks + a.T;
+        const int threads = waves * kWave > kScatterThreads ? waves * kWave : kScatterThreads;
+        const size_t lds = (size_t)(a.H / 128) * sizeof(float);
+        if (info) info[2] = LaunchInfo{blocks, threads, lds, waves};
+        if (blocks == 0) return hipSuccess;
+        k_scatter_fp8<<<dim3((unsigned)blocks), dim3(threads), lds, stream>>>(
             x, a.topk_idx, a.tile_rank, a.tile_counts, a.expert_counts, a.expert_offsets, a.T,
             a.H, a.E, a.k, a.max_rows, (int)pad_blocks, pad_per_expert, pad_rows_per_block, out,
             a.out_scales, a.row_src, a.dst_row);
-    else
-        k_scatter<false><<<dim3((unsigned)blocks), dim3(kScatterThreads), 0, stream>>>(
+    } else {
+        const int units = a.H / 8;
+        const int64_t waves_per_token = (units + kWave - 1) / kWave;
+        const int64_t blocks =
+            pad_blocks + (a.T * waves_per_token + kScatterWaves - 1) / kScatterWaves;
+        if (info) info[2] = LaunchInfo{blocks, kScatterThreads, 0, waves_per_token};
+        if (blocks == 0) return hipSuccess;
+        k_scatter_bf16<<<dim3((unsigned)blocks), dim3(kScatterThreads), 0, stream>>>(
             x, a.topk_idx, a.tile_rank, a.tile_counts, a.expert_counts, a.expert_offsets, a.T,
             a.H, a.E, a.k, a.max_rows, (int)pad_blocks, pad_per_expert, pad_rows_per_block, out,
-            a.out_scales, a.row_src, a.dst_row);
+            a.row_src, a.dst_row);
+    }
     return hipGetLastError();
 }
 

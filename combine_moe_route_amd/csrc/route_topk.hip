@@ -68,8 +68,10 @@ struct FAdd {
 
 }  // namespace
 
+constexpr int kRouteThreads = 256;
+
 template <int S, int NV>
-__global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ logits, int64_t T,
+__global__ __launch_bounds__(kRouteThreads) void k_route_topk(const float* __restrict__ logits, int64_t T,
                                                     int E, int k, int32_t* __restrict__ topk_idx,
                                                     float* __restrict__ topk_w) {
     constexpr uint32_t kNone = 0xFFFFFFFFu;
@@ -77,18 +79,30 @@ __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ lo
     const int g = lane & (S - 1);
     const int base = lane & ~(S - 1);          // first lane of this group
     constexpr int kTokensPerWave = kWave / S;
-    const int64_t wave = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
+    const int64_t wave = (int64_t)blockIdx.x * (kRouteThreads / kWave) +
+                         __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
     const int64_t t = wave * kTokensPerWave + lane / S;
     const bool live = t < T;
 
     // candidates as order keys (unsigned order == numeric order, -0 == +0);
     // 0 marks an empty slot, real keys are never 0
     uint32_t c[NV];
-    const float* row = logits + (live ? t : 0) * (int64_t)E;
+    if constexpr (S == kWave) {
+        // one token per wave: the row goes through a wave-uniform range
+        // descriptor, so all NV loads issue back to back (lanes past the row,
+        // or a token past T, read 0)
+        const auto rs = range_rsrc(logits + (live ? t : 0) * (int64_t)E, live ? 4 * E : 0);
+        uint32_t bits[NV];   // raw fp32 bit patterns
 #pragma unroll
-    for (int i = 0; i < NV; i++) {
-        const int e = g + S * i;
-        c[i] = (live && e < E) ? order_key(row[e]) : 0u;
+        for (int i = 0; i < NV; i++)
+            bits[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (g + S * i), 0, 0);
+#pragma unroll
+        for (int i = 0; i < NV; i++)
+            c[i] = (live && g + S * i < E) ? order_key(__uint_as_float(bits[i])) : 0u;
+    } else {
+        // several tokens per wave, one candidate per lane
+        static_assert(NV == 1, "groups narrower than a wave hold one candidate per lane");
+        c[0] = (live && g < E) ? order_key(logits[t * (int64_t)E + g]) : 0u;
     }
 
     uint32_t sel_key[NV];
@@ -173,7 +187,7 @@ __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ lo
 template <int S, int NV>
 static void launch_s(const float* logits, int64_t T, int E, int k, int32_t* topk_idx,
                      float* topk_w, hipStream_t stream, int64_t blocks) {
-    k_route_topk<S, NV><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(logits, T, E, k, topk_idx,
+    k_route_topk<S, NV><<<dim3((unsigned)blocks), dim3(kRouteThreads), 0, stream>>>(logits, T, E, k, topk_idx,
                                                                         topk_w);
 }
 
@@ -183,7 +197,7 @@ hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k,
     int S = 1;
     while (S < E && S < kWave) S <<= 1;
     const int nv = (E + S - 1) / S;
-    const int threads = 256;
+    const int threads = kRouteThreads;
     const int64_t tokens_per_block = (threads / kWave) * (kWave / S);
     const int64_t blocks = (T + tokens_per_block - 1) / tokens_per_block;
     if (info) *info = LaunchInfo{blocks, threads, 0, S};
