@@ -19,8 +19,8 @@
 //   3. a ballot of the lanes holding that maximum names the winner; if several
 //      lanes tie, a second butterfly takes the smallest expert index,
 //   4. the winning lane retires that candidate.
-// Round r's winner is kept by lane r % S in register slot r / S, which then
-// writes slot r of the output.
+// Round r's winner is kept by lane r (by lane r % 64 in register r / 64 when
+// k > 64), which then writes slot r of the output.
 #include "moe_device.h"
 #include "launch.h"
 
@@ -105,81 +105,102 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_topk(const float* __res
         c[0] = (live && g < E) ? order_key(logits[t * (int64_t)E + g]) : 0u;
     }
 
-    uint32_t sel_key[NV];
-    int sel_e[NV];
-#pragma unroll
-    for (int i = 0; i < NV; i++) {
-        sel_key[i] = 0u;
-        sel_e[i] = 0;
-    }
-    uint32_t first = 0u;
-
-    for (int r = 0; r < k; r++) {
-        // best remaining candidate of this lane (strict >: ties keep the lower slot)
-        uint32_t best = c[0];
-        int bslot = 0;
-#pragma unroll
-        for (int i = 1; i < NV; i++)
-            if (c[i] > best) {
-                best = c[i];
-                bslot = i;
-            }
-        const uint32_t bidx = best == 0u ? kNone : (uint32_t)(g + S * bslot);
-        // group maximum, then who holds it
-        const uint32_t m = group_reduce<S>(best, UMax());
-        const bool holds = best == m && best != 0u;
-        const uint64_t mask = __ballot(holds);
-        const uint64_t gmask = (S == kWave) ? mask : (mask >> base) & ((1ull << S) - 1ull);
-        uint32_t we;
-        if (NV == 1) {
-            // one candidate per lane: the lowest holding lane is the lowest expert
-            we = gmask ? (uint32_t)__builtin_ctzll(gmask) : 0u;
-        } else if (__popcll(gmask) <= 1) {
-            // S == 64 here, so the holder is wave-uniform
-            const int wl = gmask ? (int)__builtin_ctzll(gmask) : 0;
-            we = (uint32_t)__builtin_amdgcn_readlane((int)bidx, wl);
-        } else {
-            we = group_reduce<S>(holds ? bidx : kNone, UMin());
-        }
-        if (r == 0) first = m;
-        // retire the winner
-        if ((int)(we & (S - 1)) == g) {
-            const int slot = (int)(we / S);
-#pragma unroll
-            for (int i = 0; i < NV; i++)
-                if (i == slot) c[i] = 0u;
-        }
-        // record round r
-        if ((r & (S - 1)) == g) {
-            const int slot = r / S;
-#pragma unroll
-            for (int i = 0; i < NV; i++)
-                if (i == slot) {
-                    sel_key[i] = m;
-                    sel_e[i] = (int)we;
-                }
-        }
-    }
-
-    // weights: exp(l_j - l_max) / sum over the chosen, fp32, true division
-    float ex[NV];
-    float part = 0.0f;
-#pragma unroll
-    for (int i = 0; i < NV; i++) {
-        const int r = g + S * i;
-        ex[i] = (r < k) ? expf(key_value(sel_key[i]) - key_value(first)) : 0.0f;
-        part += ex[i];
-    }
-    const float sum = __uint_as_float(group_reduce<S>(__float_as_uint(part), FAdd()));
-
-    if (live) {
+    if constexpr (S == kWave) {
+        // One token per wave. Round r's winner (key and expert, wave-uniform)
+        // is written into lane r of sel_key / sel_e when r < 64; rounds past
+        // 64 (only when k > 64) go to the per-slot registers below.
+        uint32_t sel_key = 0u;
+        int sel_e = 0;
+        uint32_t hi_key[NV];
+        int hi_e[NV];
 #pragma unroll
         for (int i = 0; i < NV; i++) {
-            const int r = g + S * i;
-            if (r < k) {
-                topk_idx[t * k + r] = sel_e[i];
-                topk_w[t * k + r] = ex[i] / sum;
+            hi_key[i] = 0u;
+            hi_e[i] = 0;
+        }
+        uint32_t first = 0u;
+        for (int r = 0; r < k; r++) {
+            uint32_t best = c[0];
+#pragma unroll
+            for (int i = 1; i < NV; i++) best = best > c[i] ? best : c[i];
+            const uint32_t m = group_reduce<S>(best, UMax());
+            const uint64_t mask = __ballot(best == m);
+            // the holding lane's first slot with the maximum (lowest expert)
+            int slot = NV - 1;
+#pragma unroll
+            for (int i = NV - 2; i >= 0; i--) slot = c[i] == m ? i : slot;
+            int we;
+            if (__popcll(mask) == 1) {
+                const int wl = (int)__builtin_ctzll(mask);
+                we = wl + S * __builtin_amdgcn_readlane(slot, wl);
+            } else {
+                // several lanes hold the maximum: the smallest expert index wins
+                we = (int)group_reduce<S>(best == m ? (uint32_t)(g + S * slot) : kNone, UMin());
             }
+            const int clear = (lane == (we & (S - 1))) ? (int)((uint32_t)we / S) : NV;
+#pragma unroll
+            for (int i = 0; i < NV; i++) c[i] = (i == clear) ? 0u : c[i];
+            if (r == 0) first = m;
+            if (r < kWave) {
+                sel_key = lane == r ? m : sel_key;
+                sel_e = lane == r ? we : sel_e;
+            } else if (lane == (r & (kWave - 1))) {
+#pragma unroll
+                for (int i = 1; i < NV; i++)
+                    if (i == r / kWave) {
+                        hi_key[i] = m;
+                        hi_e[i] = we;
+                    }
+            }
+        }
+        // weights: exp(l_j - l_max) / sum over the chosen, fp32, true division
+        const float lmax = key_value(first);
+        const float ex0 = lane < k ? expf(key_value(sel_key) - lmax) : 0.0f;
+        float part = ex0;
+        float exh[NV];
+#pragma unroll
+        for (int i = 1; i < NV; i++) {
+            exh[i] = (lane + kWave * i < k) ? expf(key_value(hi_key[i]) - lmax) : 0.0f;
+            part += exh[i];
+        }
+        const float sum = __uint_as_float(group_reduce<S>(__float_as_uint(part), FAdd()));
+        if (live) {
+            if (lane < k) {
+                topk_idx[t * k + lane] = sel_e;
+                topk_w[t * k + lane] = ex0 / sum;
+            }
+#pragma unroll
+            for (int i = 1; i < NV; i++) {
+                const int r = lane + kWave * i;
+                if (r < k) {
+                    topk_idx[t * k + r] = hi_e[i];
+                    topk_w[t * k + r] = exh[i] / sum;
+                }
+            }
+        }
+    } else {
+        // Groups narrower than a wave: one candidate per lane, so the lowest
+        // holding lane of a group is its lowest expert.
+        uint32_t sel_key = 0u;
+        int sel_e = 0;
+        uint32_t first = 0u;
+        for (int r = 0; r < k; r++) {
+            const uint32_t m = group_reduce<S>(c[0], UMax());
+            const uint64_t mask = __ballot(c[0] == m && c[0] != 0u);
+            const uint64_t gmask = (mask >> base) & ((1ull << S) - 1ull);
+            const int we = gmask ? (int)__builtin_ctzll(gmask) : 0;
+            if (g == we) c[0] = 0u;
+            if (r == 0) first = m;
+            if (g == r) {
+                sel_key = m;
+                sel_e = we;
+            }
+        }
+        const float ex = g < k ? expf(key_value(sel_key) - key_value(first)) : 0.0f;
+        const float sum = __uint_as_float(group_reduce<S>(__float_as_uint(ex), FAdd()));
+        if (live && g < k) {
+            topk_idx[t * k + g] = sel_e;
+            topk_w[t * k + g] = ex / sum;
         }
     }
 }
