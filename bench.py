@@ -9,8 +9,12 @@ Before every step a 1 GiB scratch buffer is written so the step starts with
 a cold Infinity Cache; that write is outside the timed events. Dispatch and
 combine are timed with HIP events on the stream the kernels are launched on.
 
+Each timed step is bracketed by one pair of events (an event marker in the
+middle of the stream leaves a bubble of a few microseconds, so the per-part
+split is measured in a second pass with markers between the parts).
+
 Prints one JSON line. value = effective HBM GB/s = algorithmic bytes of
-dispatch + combine / (dispatch + combine time), median over steps.
+dispatch + combine / step time, median over steps.
 """
 from __future__ import annotations
 
@@ -97,18 +101,20 @@ def run_gpu(w, steps, warmup, cold=True):
     R = int(bufs.expert_offsets[-1].item())
 
     stream = torch.cuda.current_stream(dev)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
 
-    def step(e=None):
+    def step(e=None, split=False):
+        # e: events [start, after route, after dispatch, end]; the inner two
+        # are recorded only when split is set, because every event marker
+        # leaves a few-microsecond bubble in the stream
         if cold:
             scratch.fill_(1)
         if e is not None:
             e[0].record(stream)
         moe_route_topk(logits, w.k, topk_idx, topk_w)
-        if e is not None:
+        if split:
             e[1].record(stream)
         moe_dispatch(x, topk_idx, w.E, w.groups, w.row_align, w.fp8, bufs)
-        if e is not None:
+        if split:
             e[2].record(stream)
         moe_combine(expert_out, bufs.dst_row, topk_w, y)
         if e is not None:
@@ -116,17 +122,25 @@ def run_gpu(w, steps, warmup, cold=True):
 
     for _ in range(warmup):
         step()
+    # timed steps: one event pair per step
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         step(ev[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-
-    route = [a[0].elapsed_time(a[1]) * 1e3 for a in ev]       # microseconds
-    disp = [a[1].elapsed_time(a[2]) * 1e3 for a in ev]
-    comb = [a[2].elapsed_time(a[3]) * 1e3 for a in ev]
-    return dict(R=R, route=route, disp=disp, comb=comb, wall_s=wall)
+    total = [a[0].elapsed_time(a[3]) * 1e3 for a in ev]           # microseconds
+    # split steps: route / dispatch / combine intervals (combine's interval is
+    # the combine kernel alone: its start marker follows dispatch's last kernel)
+    sp = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for i in range(steps):
+        step(sp[i], split=True)
+    torch.cuda.synchronize()
+    route = [a[0].elapsed_time(a[1]) * 1e3 for a in sp]
+    disp = [a[1].elapsed_time(a[2]) * 1e3 for a in sp]
+    comb = [a[2].elapsed_time(a[3]) * 1e3 for a in sp]
+    return dict(R=R, total=total, route=route, disp=disp, comb=comb, wall_s=wall)
 
 
 def copy_bandwidth(nbytes=1 << 30, reps=10):
@@ -173,7 +187,7 @@ def cpu_baseline(w, max_tokens):
 
 def summarize(w, r):
     bd, bc = algorithmic_bytes(w.T, w.H, w.E, w.k, r["R"], w.fp8)
-    tot = [a + b + c for a, b, c in zip(r["route"], r["disp"], r["comb"])]
+    tot = r["total"]
     dmed = statistics.median([a + b for a, b in zip(r["route"], r["disp"])])
     cmed = statistics.median(r["comb"])
     tmed = statistics.median(tot)

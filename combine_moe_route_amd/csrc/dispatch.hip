@@ -66,10 +66,17 @@ __global__ __launch_bounds__(kTileTokens) void k_tile_hist(const int32_t* __rest
     __syncthreads();
 
     // expert ids are loaded in batches of 8 before any LDS atomic, so the
-    // loads are in flight together
+    // loads are in flight together; the first batch stays in registers for
+    // the ranking pass
     const uint64_t bit = 1ull << lane;
+    int e0[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; jj++) e0[jj] = (live && jj < k) ? topk_idx[t * k + jj] : -1;
+#pragma unroll
+    for (int jj = 0; jj < 8; jj++)
+        if ((unsigned)e0[jj] < (unsigned)E) atomicOr(&mask[w * E + e0[jj]], bit);
     if (live) {
-        for (int j0 = 0; j0 < k; j0 += 8) {
+        for (int j0 = 8; j0 < k; j0 += 8) {
             int e[8];
 #pragma unroll
             for (int jj = 0; jj < 8; jj++) e[jj] = (j0 + jj < k) ? topk_idx[t * k + j0 + jj] : -1;
@@ -96,7 +103,8 @@ __global__ __launch_bounds__(kTileTokens) void k_tile_hist(const int32_t* __rest
         for (int j0 = 0; j0 < k; j0 += 8) {
             int e[8];
 #pragma unroll
-            for (int jj = 0; jj < 8; jj++) e[jj] = (j0 + jj < k) ? topk_idx[t * k + j0 + jj] : -1;
+            for (int jj = 0; jj < 8; jj++)
+                e[jj] = j0 == 0 ? e0[jj] : ((j0 + jj < k) ? topk_idx[t * k + j0 + jj] : -1);
 #pragma unroll
             for (int jj = 0; jj < 8; jj++) {
                 if (j0 + jj >= k) break;
@@ -152,10 +160,16 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(int32_t* __restrict__ til
     const int64_t b0 = min(tiles, (int64_t)p * per);
     const int64_t b1 = min(tiles, b0 + per);
 
-    // pass 1: rows of this expert in tiles [b0, b1)
+    // pass 1: rows of this expert in tiles [b0, b1); the first 8 counts stay
+    // in registers for pass 2
     int part = 0;
+    int c0[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) c0[i] = (real && b0 + i < b1) ? tile_counts[(b0 + i) * E + e] : 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) part += c0[i];
     if (real) {
-        for (int64_t b = b0; b < b1; b += 8) {
+        for (int64_t b = b0 + 8; b < b1; b += 8) {
             int c[8];
 #pragma unroll
             for (int i = 0; i < 8; i++) c[i] = (b + i < b1) ? tile_counts[(b + i) * E + e] : 0;
@@ -204,7 +218,8 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(int32_t* __restrict__ til
         for (int64_t b = b0; b < b1; b += 8) {
             int c[8];
 #pragma unroll
-            for (int i = 0; i < 8; i++) c[i] = (b + i < b1) ? tile_counts[(b + i) * E + e] : 0;
+            for (int i = 0; i < 8; i++)
+                c[i] = b == b0 ? c0[i] : ((b + i < b1) ? tile_counts[(b + i) * E + e] : 0);
 #pragma unroll
             for (int i = 0; i < 8; i++)
                 if (b + i < b1) {
