@@ -55,15 +55,17 @@ def src_hash(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def read_traffic(kernel_tag, workload, src_path):
-    """HBM traffic per launch from a committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
-    p = os.path.join(PROFILES, f"{kernel_tag}_{workload}_counters.md")
+def read_traffic(kernel, workload, src_path):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (profiles/counters_<workload>.md: FETCH_SIZE and WRITE_SIZE scaled
+    by a 1 GiB copy), if the counters were taken on the current kernel source;
+    else None."""
+    p = os.path.join(PROFILES, f"counters_{workload}.md")
     if not os.path.exists(p):
         return None
     text = open(p).read()
-    m = re.search(r"source_sha256_16:\s*([0-9a-f]{16})", text)
-    t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    m = re.search(rf"{kernel} source_sha256_16:\s*([0-9a-f]{{16}})", text)
+    t = re.search(rf"{kernel} traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not m or not t or m.group(1) != src_hash(src_path):
         return None
     return float(t.group(1))
@@ -249,7 +251,7 @@ def main():
 
     comb_avg_us = statistics.mean(r["comb"])
     achieved = s["bytes_combine"] / (comb_avg_us * 1e-6) / 1e9
-    traffic = read_traffic("combine", w.name, COMBINE_SRC)
+    traffic = read_traffic("k_combine", w.name, COMBINE_SRC)
 
     out = {
         "metric": "dispatch+combine µs and effective HBM GB/s (% of peak), 1 MI355X",

@@ -254,3 +254,22 @@ def test_router_every_group_width(dev, E):
     for k in ks:
         route_parity(l, k, dev)
         route_parity(lt.astype(np.float32), k, dev)
+
+
+@pytest.mark.parametrize("E,k", [(128, 65), (128, 128), (300, 100), (1024, 200), (1024, 1024),
+                                 (65, 65), (777, 129)])
+def test_router_more_than_64_experts_per_token(dev, E, k):
+    """Rounds past the 64th are kept in per-slot registers of the lanes."""
+    l = gen_logits(200, E, seed=E + k)
+    route_parity(l, k, dev)
+    route_parity((np.round(l * 2) / 2).astype(np.float32), k, dev)
+
+
+@pytest.mark.parametrize("c", [
+    Case(T=300, H=512, E=128, k=65, groups=4, row_align=8, seed=21),                 # bf16, k > 64
+    Case(T=257, H=1024, E=64, k=12, groups=8, row_align=128, fp8=True, seed=22),     # FP8, k > 8
+    Case(T=100, H=256, E=512, k=100, groups=16, row_align=4, fp8=True, seed=23),     # FP8, k > 64
+    Case(T=50, H=20480, E=16, k=4, groups=2, row_align=2, fp8=True, seed=24),        # FP8, > 16 waves per row
+], ids=lambda c: c.label())
+def test_many_slots_and_wide_rows(dev, c):
+    full_case(c, dev)
