@@ -38,6 +38,13 @@ int64_t max_rows_of(int64_t T, int E, int k, int row_align) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 
+// Row kernels launch one 64-lane wave per (token, 512 bytes of a bf16 row),
+// four waves per block; keep every grid within the 2^31 - 1 block limit.
+bool row_grid_fits(int64_t T, int H) {
+    const int64_t waves_per_token = ((int64_t)H * 2 / 16 + 63) / 64;
+    return T * waves_per_token / 4 + 1 < kInt32Max;
+}
+
 }  // namespace
 
 extern "C" {
@@ -79,6 +86,7 @@ int moe_dispatch(const void* x, const int32_t* topk_idx, int64_t T, int H, int E
     if (out_dtype != MOE_OUT_BF16 && out_dtype != MOE_OUT_FP8_E4M3) return MOE_EINVAL;
     const bool fp8 = out_dtype == MOE_OUT_FP8_E4M3;
     if (H < 1 || H > 65536 || H % (fp8 ? 128 : 8) != 0) return MOE_EINVAL;
+    if (!row_grid_fits(T, H)) return MOE_EINVAL;
     // required pointers
     if (!expert_counts || !expert_offsets) return MOE_ENULL;
     if (T > 0 && (!x || !topk_idx || !dst_row)) return MOE_ENULL;
@@ -132,6 +140,7 @@ int moe_combine(const void* expert_out, const int32_t* dst_row, const float* top
     if (T < 0 || k < 1 || k > MOE_MAX_EXPERTS || H < 1 || H > 65536 || H % 8 != 0)
         return MOE_EINVAL;
     if (T > kInt32Max || T * (int64_t)k > kInt32Max) return MOE_EINVAL;
+    if (!row_grid_fits(T, H)) return MOE_EINVAL;
     if (T == 0) return MOE_OK;
     if (!expert_out || !dst_row || !topk_w || !y) return MOE_ENULL;
     if (!aligned(expert_out, 16) || !aligned(y, 16)) return MOE_EALIGN;

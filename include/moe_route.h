@@ -102,7 +102,8 @@ size_t moe_dispatch_workspace_bytes(int64_t T, int E, int k, int groups);
  *   topk_idx       device, int32 [T, k]; an id outside [0, E) drops that slot
  *                  (not counted, dst_row = -1, no row written)
  *   T, H, E, k     1 <= k <= E <= MOE_MAX_EXPERTS; H % 8 == 0 (bf16) or
- *                  H % 128 == 0 (FP8); 1 <= H <= 65536
+ *                  H % 128 == 0 (FP8); 1 <= H <= 65536; T * k < 2^31 and
+ *                  T * ceil(H / 256) < 2^33 (launch-grid limit)
  *   groups         destination groups (1 = none), E % groups == 0; group g
  *                  holds experts [g*E/groups, (g+1)*E/groups), so its rows
  *                  form one contiguous send buffer
@@ -147,7 +148,8 @@ int moe_dispatch(const void* x, const int32_t* topk_idx,
  *   dst_row     device int32 [T, k]; a negative entry contributes nothing
  *   topk_w      device fp32 [T, k]
  *   y           device bf16 [T, H] out, 16-byte aligned
- *   H % 8 == 0, 1 <= H <= 65536, 1 <= k <= MOE_MAX_EXPERTS, T >= 0.
+ *   H % 8 == 0, 1 <= H <= 65536, 1 <= k <= MOE_MAX_EXPERTS, T >= 0,
+ *   T * k < 2^31, T * ceil(H / 256) < 2^33 (launch-grid limit).
  */
 int moe_combine(const void* expert_out, const int32_t* dst_row,
                 const float* topk_w, int64_t T, int H, int k,

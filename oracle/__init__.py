@@ -60,6 +60,8 @@ def _load():
     lib.oracle_bf16_from_double.restype = ctypes.c_uint16
     lib.oracle_quantize_block.argtypes = [P, P, P]
     lib.oracle_quantize_block.restype = None
+    lib.oracle_combine_sender.argtypes = [P, P, P, P, i64, i32, i32, i32, i32, P, P, P]
+    lib.oracle_combine_sender.restype = None
     lib.oracle_e4m3_encode_array.argtypes = [P, P, i64]
     lib.oracle_e4m3_encode_array.restype = None
     lib.oracle_e4m3_encode_bits.argtypes = [ctypes.c_uint32, i64, P]
@@ -150,6 +152,24 @@ def combine(expert_out: np.ndarray, dst_row: np.ndarray, topk_w: np.ndarray) -> 
     y = np.empty((T, H), np.uint16)
     _load().oracle_combine(_p(expert_out), _p(dst_row), _p(topk_w), T, H, k, _p(y))
     return y
+
+
+def combine_sender(expert_out: np.ndarray, dst_row: np.ndarray, topk_w: np.ndarray,
+                   topk_idx: np.ndarray, E: int, groups: int):
+    """Sender-side partial reduction: (partial uint16 [T,k,H], count int32 [T],
+    y uint16 [T,H]); rows of partial past count[t] are zero."""
+    expert_out = _c(expert_out, np.uint16)
+    dst_row = _c(dst_row, np.int32)
+    topk_w = _c(topk_w, np.float32)
+    topk_idx = _c(topk_idx, np.int32)
+    T, k = dst_row.shape
+    H = expert_out.shape[1]
+    partial = np.zeros((T, k, H), np.uint16)
+    count = np.empty(T, np.int32)
+    y = np.empty((T, H), np.uint16)
+    _load().oracle_combine_sender(_p(expert_out), _p(dst_row), _p(topk_w), _p(topk_idx), T, H,
+                                  E, k, groups, _p(partial), _p(count), _p(y))
+    return partial, count, y
 
 
 def e4m3_encode(v: float) -> int:

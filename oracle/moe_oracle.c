@@ -317,3 +317,56 @@ void oracle_e4m3_encode_bits(uint32_t start, int64_t count, uint8_t* out) {
         out[i] = oracle_e4m3_encode(f);
     }
 }
+
+/* ---------------------------------------------------------------- sender-side */
+
+/* Combine with partial sums on the sending side ([EFA] Evaluation: the
+ * sender accumulates to cut the bytes transferred, at a possible cost in
+ * accuracy; here a destination group stands for the sending rank). For token
+ * t the distinct groups g = topk_idx[t,j] / (E/G) of its live slots are taken
+ * in ascending order; partial row p of t is
+ *   P[t,p] = bf16( sum over slots j of group g_p, in slot order, of w[t,j] * eo[dst_row[t,j]] )
+ * (fp64 accumulation, one rounding: the row travels as bf16), and
+ *   y[t] = bf16( sum over p of P[t,p] )  (fp64, one rounding).
+ * partial has room for k rows per token ([T, k, H]); count[t] = rows used. */
+void oracle_combine_sender(const uint16_t* expert_out, const int32_t* dst_row,
+                           const float* topk_w, const int32_t* topk_idx,
+                           int64_t T, int H, int E, int k, int groups,
+                           uint16_t* partial, int32_t* count, uint16_t* y) {
+    const int per = E / groups;
+    double* acc = (double*)malloc(sizeof(double) * (size_t)H);
+    double* tot = (double*)malloc(sizeof(double) * (size_t)H);
+    for (int64_t t = 0; t < T; t++) {
+        for (int h = 0; h < H; h++) tot[h] = 0.0;
+        int n = 0, prev = -1;
+        for (;;) {
+            int g = -1;                                   /* next larger group */
+            for (int j = 0; j < k; j++) {
+                int e = topk_idx[t * k + j];
+                if (dst_row[t * k + j] < 0 || e < 0 || e >= E) continue;
+                int gj = e / per;
+                if (gj > prev && (g < 0 || gj < g)) g = gj;
+            }
+            if (g < 0) break;
+            for (int h = 0; h < H; h++) acc[h] = 0.0;
+            for (int j = 0; j < k; j++) {
+                int e = topk_idx[t * k + j];
+                int64_t r = dst_row[t * k + j];
+                if (r < 0 || e < 0 || e >= E || e / per != g) continue;
+                for (int h = 0; h < H; h++)
+                    acc[h] += (double)topk_w[t * k + j] * (double)bf16_value(expert_out[r * H + h]);
+            }
+            uint16_t* prow = partial + (t * k + n) * (int64_t)H;
+            for (int h = 0; h < H; h++) {
+                prow[h] = oracle_bf16_from_double(acc[h]);
+                tot[h] += (double)bf16_value(prow[h]);
+            }
+            n++;
+            prev = g;
+        }
+        count[t] = n;
+        for (int h = 0; h < H; h++) y[t * H + h] = oracle_bf16_from_double(tot[h]);
+    }
+    free(acc);
+    free(tot);
+}

@@ -108,6 +108,7 @@ def test_dispatch_validation():
     assert dispatch(H=65544) == EINVAL
     assert dispatch(T=-5) == EINVAL
     assert dispatch(T=2 ** 29, k=8) == EINVAL            # rows overflow int32
+    assert dispatch(T=2 ** 27, H=65536, k=1, E=1) == EINVAL   # launch grid too large
     assert dispatch(x=None) == ENULL
     assert dispatch(idx=None) == ENULL
     assert dispatch(out=None) == ENULL
@@ -133,6 +134,7 @@ def test_combine_validation():
     assert c(k=0) == EINVAL
     assert c(k=1025) == EINVAL
     assert c(T=-1) == EINVAL
+    assert c(T=2 ** 28, H=65536, k=1) == EINVAL          # launch grid too large
     assert c(eo=None) == ENULL
     assert c(y=None) == ENULL
     assert c(eo=A + 8) == EALIGN

@@ -547,3 +547,103 @@ def test_chain_fp8_round_trip_error_bound():
     # E4M3 relative error 2^-4 (normals), subnormal floor 2^-10 * amax/448, two bf16 roundings
     bound = 2 ** -4 * np.abs(xf) + 2 ** -10 * amax / 448 + 2 ** -7 * np.abs(xf)
     assert np.all(np.abs(y - xf) <= bound)
+
+
+# ----------------------------------------------------------------- sender-side combine
+
+def _live_groups(idx, dst_row, E, G):
+    per = E // G
+    return [sorted({int(e) // per for e, r in zip(idx[t], dst_row[t]) if r >= 0 and 0 <= e < E})
+            for t in range(idx.shape[0])]
+
+
+def test_sender_single_group_equals_receiver_combine():
+    T, H, E, k = 60, 256, 16, 4
+    idx, w = _routing(T, E, k, seed=31)
+    x = gen_x_bf16(T, H, seed=31)
+    d = oracle.dispatch(x, idx, E)
+    eo = oracle.expert_scale(d, idx, E, fp8=False)
+    part, cnt, y = oracle.combine_sender(eo, d.dst_row, w, idx, E, groups=1)
+    assert np.all(cnt == 1)
+    assert np.array_equal(y, oracle.combine(eo, d.dst_row, w))
+    assert np.array_equal(part[:, 0], y) and np.all(part[:, 1:] == 0)
+
+
+def test_sender_counts_are_distinct_groups():
+    T, H, E, k = 200, 64, 32, 6
+    idx, w = _routing(T, E, k, seed=32)
+    idx[::9, 2] = -1                                   # dropped slots do not count
+    x = gen_x_bf16(T, H, seed=32)
+    d = oracle.dispatch(x, idx, E)
+    eo = oracle.expert_scale(d, idx, E, fp8=False)
+    for G in (2, 4, 8, 32):
+        _, cnt, _ = oracle.combine_sender(eo, d.dst_row, w, idx, E, G)
+        assert cnt.tolist() == [len(g) for g in _live_groups(idx, d.dst_row, E, G)]
+
+
+def test_sender_partials_are_nearest_bf16_of_group_sums():
+    """One expert per group: each partial is the nearest bf16 of w * v."""
+    T, H, E, k = 40, 128, 8, 3
+    idx, w = _routing(T, E, k, seed=33)
+    x = gen_x_bf16(T, H, seed=33)
+    d = oracle.dispatch(x, idx, E)
+    eo = oracle.expert_scale(d, idx, E, fp8=False)
+    part, cnt, _ = oracle.combine_sender(eo, d.dst_row, w, idx, E, groups=E)
+    eof = bf16_bits_to_f32(eo).astype(np.float64)
+    for t in range(T):
+        order = np.argsort(idx[t])                     # groups ascending = experts ascending
+        for p, j in enumerate(order):
+            exact = float(w[t, j]) * eof[d.dst_row[t, j]]
+            got = bf16_bits_to_f32(part[t, p]).astype(np.float64)
+            up = bf16_bits_to_f32(part[t, p] + np.uint16(1)).astype(np.float64)
+            dn = bf16_bits_to_f32(part[t, p] - np.uint16(1)).astype(np.float64)
+            err = np.abs(got - exact)
+            assert np.all((err <= np.abs(up - exact)) & (err <= np.abs(dn - exact)) | (part[t, p] & 0x7FFF == 0))
+
+
+def test_sender_equals_receiver_when_sums_are_exact():
+    """Power-of-two weights and small-integer rows make every partial exact."""
+    T, H, E, k = 30, 64, 16, 4
+    rng = np.random.default_rng(34)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    w = (2.0 ** -rng.integers(0, 4, (T, k))).astype(np.float32)
+    x = f32_to_bf16_bits(rng.integers(-8, 9, (T, H)).astype(np.float32))
+    d = oracle.dispatch(x, idx, E)
+    eo = oracle.expert_scale(d, idx, E, fp8=False, identity=True)
+    want = oracle.combine(eo, d.dst_row, w)
+    for G in (1, 2, 4, 16):
+        _, _, y = oracle.combine_sender(eo, d.dst_row, w, idx, E, G)
+        assert np.array_equal(y, want), G
+
+
+def test_sender_error_bound():
+    """|y - exact| <= (n_groups + 1) half-units of bf16 relative to the sum of |terms|."""
+    T, H, E, k = 100, 256, 64, 8
+    idx, w = _routing(T, E, k, seed=35)
+    x = gen_x_bf16(T, H, seed=35)
+    d = oracle.dispatch(x, idx, E)
+    eo = oracle.expert_scale(d, idx, E, fp8=False)
+    _, cnt, y = oracle.combine_sender(eo, d.dst_row, w, idx, E, groups=8)
+    eof = bf16_bits_to_f32(eo).astype(np.float64)
+    terms = w[:, :, None].astype(np.float64) * eof[d.dst_row]
+    exact = terms.sum(1)
+    mag = np.abs(terms).sum(1)
+    err = np.abs(bf16_bits_to_f32(y).astype(np.float64) - exact)
+    assert np.all(err <= (cnt[:, None] + 1) * 2.0 ** -8 * mag + 1e-30)
+
+
+def test_sender_receiver_half_sums_the_rounded_partials():
+    """y is the nearest bf16 of the sum of the (bf16) partial rows."""
+    T, H, E, k = 80, 128, 32, 8
+    idx, w = _routing(T, E, k, seed=36)
+    x = gen_x_bf16(T, H, seed=36)
+    d = oracle.dispatch(x, idx, E)
+    eo = oracle.expert_scale(d, idx, E, fp8=False)
+    part, cnt, y = oracle.combine_sender(eo, d.dst_row, w, idx, E, groups=8)
+    s = bf16_bits_to_f32(part).astype(np.float64).sum(1)          # unused rows are zero
+    got = bf16_bits_to_f32(y).astype(np.float64)
+    up = bf16_bits_to_f32((y + np.uint16(1)) & np.uint16(0xFFFF)).astype(np.float64)
+    dn = bf16_bits_to_f32((y - np.uint16(1)) & np.uint16(0xFFFF)).astype(np.float64)
+    err = np.abs(got - s)
+    ok = ((err <= np.abs(up - s)) & (err <= np.abs(dn - s))) | ((y & 0x7FFF) == 0)
+    assert ok.all()
