@@ -29,6 +29,8 @@ EXPORTS = (
     "moe_dispatch_workspace_bytes",
     "moe_dispatch",
     "moe_combine",
+    "moe_combine_send",
+    "moe_combine_recv",
     "moe_harness_expert_scale",
     "moe_status_string",
 )
@@ -58,6 +60,10 @@ def _load() -> ctypes.CDLL:
     lib.moe_dispatch.restype = i32
     lib.moe_combine.argtypes = [P, P, P, i64, i32, i32, P, P]
     lib.moe_combine.restype = i32
+    lib.moe_combine_send.argtypes = [P, P, P, P, i64, i32, i32, i32, i32, P, P, P]
+    lib.moe_combine_send.restype = i32
+    lib.moe_combine_recv.argtypes = [P, P, i64, i32, i32, P, P]
+    lib.moe_combine_recv.restype = i32
     lib.moe_harness_expert_scale.argtypes = [P, P, P, P, P, i64, i32, i32, i32, i32, P, P]
     lib.moe_harness_expert_scale.restype = i32
     lib.moe_status_string.argtypes = [i32]
@@ -207,6 +213,46 @@ def moe_combine(expert_out: torch.Tensor, dst_row: torch.Tensor, topk_w: torch.T
     _need(y, "y", torch.bfloat16, (T, H), dev)
     _check("moe_combine", lib.moe_combine(_ptr(expert_out), _ptr(dst_row), _ptr(topk_w), T, H, k,
                                           _ptr(y), _stream(dev)))
+    return y
+
+
+def moe_combine_send(expert_out: torch.Tensor, dst_row: torch.Tensor, topk_w: torch.Tensor,
+                     topk_idx: torch.Tensor, E: int, groups: int,
+                     partial: Optional[torch.Tensor] = None,
+                     partial_count: Optional[torch.Tensor] = None):
+    """Sending half of the sender-side partial-reduction combine:
+    (partial bf16 [T,k,H], partial_count int32 [T])."""
+    _need(expert_out, "expert_out", torch.bfloat16)
+    dev = expert_out.device
+    H = expert_out.shape[1]
+    _need(dst_row, "dst_row", torch.int32, None, dev)
+    T, k = dst_row.shape
+    _need(topk_w, "topk_w", torch.float32, (T, k), dev)
+    _need(topk_idx, "topk_idx", torch.int32, (T, k), dev)
+    if partial is None:
+        partial = torch.empty((T, k, H), dtype=torch.bfloat16, device=dev)
+    if partial_count is None:
+        partial_count = torch.empty(T, dtype=torch.int32, device=dev)
+    _need(partial, "partial", torch.bfloat16, (T, k, H), dev)
+    _need(partial_count, "partial_count", torch.int32, (T,), dev)
+    _check("moe_combine_send", lib.moe_combine_send(
+        _ptr(expert_out), _ptr(dst_row), _ptr(topk_w), _ptr(topk_idx), T, H, E, k, groups,
+        _ptr(partial), _ptr(partial_count), _stream(dev)))
+    return partial, partial_count
+
+
+def moe_combine_recv(partial: torch.Tensor, partial_count: torch.Tensor,
+                     y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Receiving half: y bf16 [T,H] = sum of the token's partial rows (fp32)."""
+    _need(partial, "partial", torch.bfloat16)
+    dev = partial.device
+    T, k, H = partial.shape
+    _need(partial_count, "partial_count", torch.int32, (T,), dev)
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _need(y, "y", torch.bfloat16, (T, H), dev)
+    _check("moe_combine_recv", lib.moe_combine_recv(_ptr(partial), _ptr(partial_count), T, H, k,
+                                                    _ptr(y), _stream(dev)))
     return y
 
 

@@ -152,6 +152,46 @@ int moe_combine(const void* expert_out, const int32_t* dst_row, const float* top
     return status_of(e);
 }
 
+int moe_combine_send(const void* expert_out, const int32_t* dst_row, const float* topk_w,
+                     const int32_t* topk_idx, int64_t T, int H, int E, int k, int groups,
+                     void* partial, int32_t* partial_count, void* stream) {
+    if (T < 0 || k < 1 || E < k || E > MOE_MAX_EXPERTS || H < 1 || H > 65536 || H % 8 != 0)
+        return MOE_EINVAL;
+    if (groups < 1 || groups > E || E % groups != 0) return MOE_EINVAL;
+    if (T > kInt32Max || T * (int64_t)k > kInt32Max) return MOE_EINVAL;
+    if (!row_grid_fits(T, H)) return MOE_EINVAL;
+    if (T == 0) return MOE_OK;
+    if (!expert_out || !dst_row || !topk_w || !topk_idx || !partial || !partial_count)
+        return MOE_ENULL;
+    if (!aligned(expert_out, 16) || !aligned(partial, 16)) return MOE_EALIGN;
+    if (!aligned(dst_row, 4) || !aligned(topk_w, 4) || !aligned(topk_idx, 4) ||
+        !aligned(partial_count, 4))
+        return MOE_EALIGN;
+    moe::LaunchInfo info;
+    const hipError_t e = moe::launch_combine_send(expert_out, dst_row, topk_w, topk_idx, T, H, E,
+                                                  k, groups, partial, partial_count,
+                                                  static_cast<hipStream_t>(stream), &info);
+    if (log_enabled()) log_launch("combine_send", info);
+    return status_of(e);
+}
+
+int moe_combine_recv(const void* partial, const int32_t* partial_count, int64_t T, int H, int k,
+                     void* y, void* stream) {
+    if (T < 0 || k < 1 || k > MOE_MAX_EXPERTS || H < 1 || H > 65536 || H % 8 != 0)
+        return MOE_EINVAL;
+    if (T > kInt32Max || T * (int64_t)k > kInt32Max) return MOE_EINVAL;
+    if (!row_grid_fits(T, H)) return MOE_EINVAL;
+    if (T == 0) return MOE_OK;
+    if (!partial || !partial_count || !y) return MOE_ENULL;
+    if (!aligned(partial, 16) || !aligned(y, 16)) return MOE_EALIGN;
+    if (!aligned(partial_count, 4)) return MOE_EALIGN;
+    moe::LaunchInfo info;
+    const hipError_t e = moe::launch_combine_recv(partial, partial_count, T, H, k, y,
+                                                  static_cast<hipStream_t>(stream), &info);
+    if (log_enabled()) log_launch("combine_recv", info);
+    return status_of(e);
+}
+
 int moe_harness_expert_scale(const void* disp, const float* disp_scales, const int32_t* row_src,
                              const int32_t* topk_idx, const int32_t* expert_offsets,
                              int64_t max_rows, int H, int E, int out_dtype, int identity,

@@ -52,6 +52,14 @@ hipError_t launch_combine(const void* expert_out, const int32_t* dst_row, const 
                           int64_t T, int H, int k, void* y, hipStream_t stream,
                           LaunchInfo* info);
 
+hipError_t launch_combine_send(const void* expert_out, const int32_t* dst_row,
+                               const float* topk_w, const int32_t* topk_idx, int64_t T, int H,
+                               int E, int k, int groups, void* partial, int32_t* count,
+                               hipStream_t stream, LaunchInfo* info);
+
+hipError_t launch_combine_recv(const void* partial, const int32_t* count, int64_t T, int H,
+                               int k, void* y, hipStream_t stream, LaunchInfo* info);
+
 hipError_t launch_expert_scale(const void* disp, const float* disp_scales,
                                const int32_t* row_src, const int32_t* topk_idx,
                                const int32_t* expert_offsets, int64_t max_rows, int H,

@@ -156,6 +156,39 @@ int moe_combine(const void* expert_out, const int32_t* dst_row,
                 void* y, void* stream);
 
 /*
+ * Combine with partial sums on the sending side, as two halves. In the
+ * expert-parallel setting each destination group is the rank hosting a range
+ * of experts; that rank pre-sums, per token, the weighted rows of the token's
+ * experts it hosts and sends one bf16 row per (token, group) instead of one
+ * row per (token, expert); the token's owner then sums the partial rows
+ * ("Enabling trillion-parameter models on AWS EFA", Evaluation: DeepEP
+ * accumulates on the sender to cut transferred bytes, which may cost
+ * accuracy; moe_combine is the receiver-only alternative).
+ *
+ * moe_combine_send
+ *   expert_out, dst_row, topk_w  as for moe_combine
+ *   topk_idx     device int32 [T, k]: the experts of the slots (as routed)
+ *   E, groups    group of expert e is e / (E / groups); E % groups == 0
+ *   partial      device bf16 [T, k, H] out, 16-byte aligned: token t's partial
+ *                rows at [t, 0 .. partial_count[t]), one per distinct group of
+ *                its live slots in ascending group order; each is the fp32 sum
+ *                (slot order) of that group's weighted rows rounded to bf16
+ *   partial_count device int32 [T] out: partial rows of each token
+ * moe_combine_recv
+ *   partial, partial_count  as written by moe_combine_send
+ *   y            device bf16 [T, H] out: bf16 of the fp32 sum of the token's
+ *                partial rows in order
+ * Limits as for moe_combine; moe_combine_send also needs 1 <= k <= E <= 1024.
+ */
+int moe_combine_send(const void* expert_out, const int32_t* dst_row,
+                     const float* topk_w, const int32_t* topk_idx,
+                     int64_t T, int H, int E, int k, int groups,
+                     void* partial, int32_t* partial_count, void* stream);
+
+int moe_combine_recv(const void* partial, const int32_t* partial_count,
+                     int64_t T, int H, int k, void* y, void* stream);
+
+/*
  * Stand-in experts for tests and the benchmark (not part of the path):
  * expert_out[r] = bf16(v * c_e) with c_e = fp32(e+1) / fp32(E) (or 1 when
  * identity != 0), e the expert of row r, v the bf16 row or, for FP8 rows,

@@ -158,10 +158,14 @@ def test_harness_validation():
 
 
 def test_binding_fails_loudly_without_library(tmp_path):
+    """Any use of the API without the HIP library raises ImportError (no CPU
+    fallback); the build module itself imports without it."""
     import subprocess
     import sys
     code = ("import os; os.environ['MOE_ROUTE_LIB']=%r\n"
-            "try:\n import combine_moe_route_amd\nexcept ImportError as e:\n print('IMPORTERROR', e)\n"
+            "import combine_moe_route_amd.build\n"
+            "try:\n from combine_moe_route_amd import moe_dispatch\n"
+            "except ImportError as e:\n print('IMPORTERROR', e)\n"
             % str(tmp_path / "missing.so"))
     r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True)
-    assert "IMPORTERROR" in r.stdout and "libmoeroute.so not found" in r.stdout
+    assert "IMPORTERROR" in r.stdout and "libmoeroute.so not found" in r.stdout, r.stderr

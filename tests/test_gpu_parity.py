@@ -273,3 +273,57 @@ def test_router_more_than_64_experts_per_token(dev, E, k):
 ], ids=lambda c: c.label())
 def test_many_slots_and_wide_rows(dev, c):
     full_case(c, dev)
+
+
+def _ulps_apart(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Distance in bf16 units between bit patterns (sign-magnitude aware)."""
+    def key(x):
+        x = x.astype(np.int32)
+        return np.where(x & 0x8000, -(x & 0x7FFF), x & 0x7FFF)
+    return np.abs(key(a) - key(b))
+
+
+@pytest.mark.parametrize("c,G", [
+    (Case(T=700, H=1024, E=256, k=8, seed=41), 32),        # DeepSeek-like groups
+    (Case(T=300, H=512, E=64, k=8, seed=42), 1),           # one group: same as receiver-only
+    (Case(T=300, H=136, E=16, k=4, seed=43), 16),          # one expert per group, ragged row
+    (Case(T=200, H=256, E=128, k=12, seed=44), 8),         # k > 8: generic path
+    (Case(T=257, H=7168, E=256, k=8, seed=45), 32),        # full hidden size
+], ids=lambda v: v.label() if isinstance(v, Case) else f"G{v}")
+def test_combine_sender_side(dev, c, G):
+    from combine_moe_route_amd import moe_combine_recv, moe_combine_send
+    log(f"[case] sender-side {c.label()} G={G}")
+    x = gen_x_bf16(c.T, c.H, c.seed)
+    idx, w = oracle.route_topk(gen_logits(c.T, c.E, c.seed), c.k)
+    idx[::5, 1] = -1                                         # some dropped slots
+    ref = oracle.dispatch(x, idx, c.E)
+    eo = oracle.expert_scale(ref, idx, c.E, fp8=False)
+    P_ref, cnt_ref, y_ref = oracle.combine_sender(eo, ref.dst_row, w, idx, c.E, G)
+    eo_d = to_dev_bf16(eo, dev)
+    dr = torch.from_numpy(ref.dst_row).to(dev)
+    P, cnt = moe_combine_send(eo_d, dr, torch.from_numpy(w).to(dev),
+                              torch.from_numpy(idx).to(dev), c.E, G)
+    y = moe_combine_recv(P, cnt)
+    # the receiving half alone, on the oracle's partial rows
+    y_iso = moe_combine_recv(to_dev_bf16(P_ref, dev), torch.from_numpy(cnt_ref).to(dev))
+    torch.cuda.synchronize()
+    cnt_g = cnt.cpu().numpy()
+    assert np.array_equal(cnt_g, cnt_ref)
+    Pg = bf16_to_np(P)
+    live = np.arange(c.k)[None, :] < cnt_ref[:, None]
+    d = _ulps_apart(Pg[live], P_ref[live])
+    assert d.max() <= 1, f"partial rows differ by {d.max()} ulp"
+    log(f"  partial rows bit-exact {np.mean(d == 0):.5f}; rows per token "
+        f"{cnt_ref.mean():.2f} of k={c.k}")
+    assert _ulps_apart(bf16_to_np(y_iso), y_ref).max() <= 1
+    ok, _, exact = combine_within_tolerance(bf16_to_np(y), y_ref)
+    assert ok.all()
+    assert _ulps_apart(bf16_to_np(y), y_ref).max() <= 2
+    # accuracy consequence: distance from the exact weighted sum, both ways
+    eof = bf16_bits_to_f32(eo).astype(np.float64)
+    wl = np.where(ref.dst_row >= 0, w, 0).astype(np.float64)
+    exact_sum = (wl[:, :, None] * eof[np.maximum(ref.dst_row, 0)]).sum(1)
+    recv = bf16_bits_to_f32(oracle.combine(eo, ref.dst_row, w)).astype(np.float64)
+    send = bf16_bits_to_f32(y_ref).astype(np.float64)
+    log(f"  mean |error|: receiver-only {np.mean(np.abs(recv - exact_sum)):.3e}, "
+        f"sender-side {np.mean(np.abs(send - exact_sum)):.3e}")
