@@ -75,7 +75,7 @@ def pct(a, q):
     return float(np.percentile(np.asarray(a), q))
 
 
-def run_gpu(w, steps, warmup, cold=True):
+def run_gpu(w, steps, warmup, cold=True, sender=False):
     import torch
 
     from combine_moe_route_amd import (alloc_dispatch, moe_combine, moe_dispatch,
@@ -142,7 +142,55 @@ def run_gpu(w, steps, warmup, cold=True):
     route = [a[0].elapsed_time(a[1]) * 1e3 for a in sp]
     disp = [a[1].elapsed_time(a[2]) * 1e3 for a in sp]
     comb = [a[2].elapsed_time(a[3]) * 1e3 for a in sp]
-    return dict(R=R, total=total, route=route, disp=disp, comb=comb, wall_s=wall)
+    out = dict(R=R, total=total, route=route, disp=disp, comb=comb, wall_s=wall)
+    if sender and w.groups > 1:
+        out["sender"] = run_sender(w, steps, cold, scratch, stream, expert_out, bufs, topk_idx,
+                                   topk_w, y)
+    return out
+
+
+def run_sender(w, steps, cold, scratch, stream, expert_out, bufs, topk_idx, topk_w, y_recv):
+    """Combine with sender-side partial sums (one bf16 row per token and
+    destination group), timed like the main path, with its wire bytes and its
+    error against the exact weighted sum on a token sample."""
+    import torch
+
+    from combine_moe_route_amd import moe_combine_recv, moe_combine_send
+    dev = expert_out.device
+    partial = torch.empty((w.T, w.k, w.H), dtype=torch.bfloat16, device=dev)
+    count = torch.empty(w.T, dtype=torch.int32, device=dev)
+    y = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(-2, steps):
+        if cold:
+            scratch.fill_(1)
+        if i >= 0:
+            ev[i][0].record(stream)
+        moe_combine_send(expert_out, bufs.dst_row, topk_w, topk_idx, w.E, w.groups, partial, count)
+        if i >= 0:
+            ev[i][1].record(stream)
+        moe_combine_recv(partial, count, y)
+        if i >= 0:
+            ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    send = statistics.median([a[0].elapsed_time(a[1]) * 1e3 for a in ev])
+    recv = statistics.median([a[1].elapsed_time(a[2]) * 1e3 for a in ev])
+    rows = int(count.sum().item())
+    # error of both variants against the exact sum, on 256 sampled tokens
+    g = torch.Generator().manual_seed(0)
+    toks = torch.randperm(w.T, generator=g)[:256].to(dev)
+    dr = bufs.dst_row[toks].long()
+    live = (dr >= 0)
+    rowsv = expert_out[dr.clamp(min=0)].double()
+    wts = torch.where(live, topk_w[toks].double(), torch.zeros((), dtype=torch.float64, device=dev))
+    exact = (wts[:, :, None] * rowsv).sum(1)
+    err_recv = (y_recv[toks].double() - exact).abs().mean().item()
+    err_send = (y[toks].double() - exact).abs().mean().item()
+    return dict(us_send=round(send, 2), us_recv=round(recv, 2), us_total=round(send + recv, 2),
+                wire_rows=rows, wire_rows_receiver_only=int((bufs.dst_row >= 0).sum().item()),
+                wire_bytes=rows * 2 * w.H,
+                wire_saving=round(1 - rows / max(1, int((bufs.dst_row >= 0).sum().item())), 4),
+                mean_abs_err=err_send, mean_abs_err_receiver_only=err_recv)
 
 
 def copy_bandwidth(nbytes=1 << 30, reps=10):
@@ -238,7 +286,7 @@ def main():
     w = WORKLOADS[args.workload]
     print(f"[bench] {w.name}: T={w.T} H={w.H} E={w.E} k={w.k} G={w.groups} A={w.row_align} "
           f"fp8={w.fp8} steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
-    r = run_gpu(w, args.steps, args.warmup, cold=not args.warm)
+    r = run_gpu(w, args.steps, args.warmup, cold=not args.warm, sender=True)
     s = summarize(w, r)
     print(f"[bench] {json.dumps(s)}", file=sys.stderr, flush=True)
 
@@ -281,6 +329,7 @@ def main():
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic, "us_avg": round(comb_avg_us, 2)},
         "other": others,
+        "next": {"sender_side_combine": r.get("sender")},
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
