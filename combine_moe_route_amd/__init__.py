@@ -20,7 +20,9 @@ _API = (
     "moe_dispatch_max_rows",
     "moe_dispatch_workspace_bytes",
     "moe_harness_expert_scale",
+    "moe_route_replicas",
     "moe_route_topk",
+    "moe_route_topk_shared",
     "status_string",
 )
 

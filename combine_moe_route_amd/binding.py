@@ -25,6 +25,8 @@ MOE_MAX_EXPERTS = 1024
 # every symbol include/moe_route.h declares
 EXPORTS = (
     "moe_route_topk",
+    "moe_route_topk_shared",
+    "moe_route_replicas",
     "moe_dispatch_max_rows",
     "moe_dispatch_workspace_bytes",
     "moe_dispatch",
@@ -51,6 +53,10 @@ def _load() -> ctypes.CDLL:
     P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.moe_route_topk.argtypes = [P, i64, i32, i32, P, P, P]
     lib.moe_route_topk.restype = i32
+    lib.moe_route_topk_shared.argtypes = [P, i64, i32, i32, i32, ctypes.c_float, P, P, P]
+    lib.moe_route_topk_shared.restype = i32
+    lib.moe_route_replicas.argtypes = [P, i64, i32, i32, P, P]
+    lib.moe_route_replicas.restype = i32
     lib.moe_dispatch_max_rows.argtypes = [i64, i32, i32, i32]
     lib.moe_dispatch_max_rows.restype = i64
     lib.moe_dispatch_workspace_bytes.argtypes = [i64, i32, i32, i32]
@@ -121,6 +127,38 @@ def moe_route_topk(logits: torch.Tensor, k: int, topk_idx: Optional[torch.Tensor
     _check("moe_route_topk", lib.moe_route_topk(_ptr(logits), T, E, k, _ptr(topk_idx),
                                                 _ptr(topk_w), _stream(dev)))
     return topk_idx, topk_w
+
+
+def moe_route_topk_shared(logits: torch.Tensor, k: int, n_shared: int, shared_w: float = 1.0,
+                          topk_idx: Optional[torch.Tensor] = None,
+                          topk_w: Optional[torch.Tensor] = None):
+    """Routed top-k plus n_shared always-chosen experts E..E+n_shared-1:
+    (topk_idx int32 [T,k+n_shared], topk_w float32 [T,k+n_shared])."""
+    _need(logits, "logits", torch.float32)
+    T, E = logits.shape
+    dev = logits.device
+    ks = k + n_shared
+    if topk_idx is None:
+        topk_idx = torch.empty((T, ks), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, ks), dtype=torch.float32, device=dev)
+    _need(topk_idx, "topk_idx", torch.int32, (T, ks), dev)
+    _need(topk_w, "topk_w", torch.float32, (T, ks), dev)
+    _check("moe_route_topk_shared", lib.moe_route_topk_shared(
+        _ptr(logits), T, E, k, n_shared, float(shared_w), _ptr(topk_idx), _ptr(topk_w),
+        _stream(dev)))
+    return topk_idx, topk_w
+
+
+def moe_route_replicas(topk_idx: torch.Tensor, E: int, replica_base: torch.Tensor) -> torch.Tensor:
+    """In place: logical expert ids -> physical replica ids (copy t mod count)."""
+    _need(topk_idx, "topk_idx", torch.int32)
+    dev = topk_idx.device
+    T, k = topk_idx.shape
+    _need(replica_base, "replica_base", torch.int32, (E + 1,), dev)
+    _check("moe_route_replicas", lib.moe_route_replicas(_ptr(topk_idx), T, k, E,
+                                                        _ptr(replica_base), _stream(dev)))
+    return topk_idx
 
 
 # ----------------------------------------------------------------- dispatch

@@ -57,10 +57,37 @@ int moe_route_topk(const float* logits, int64_t T, int E, int k, int32_t* topk_i
     if (!logits || !topk_idx || !topk_w) return MOE_ENULL;
     if (!aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4)) return MOE_EALIGN;
     moe::LaunchInfo info;
-    const hipError_t e = moe::launch_route_topk(logits, T, E, k, topk_idx, topk_w,
+    const hipError_t e = moe::launch_route_topk(logits, T, E, k, 0, 0.0f, topk_idx, topk_w,
                                                 static_cast<hipStream_t>(stream), &info);
     if (log_enabled()) log_launch("route_topk", info);
     return status_of(e);
+}
+
+int moe_route_topk_shared(const float* logits, int64_t T, int E, int k, int n_shared,
+                          float shared_w, int32_t* topk_idx, float* topk_w, void* stream) {
+    if (T < 0 || k < 1 || E < k || n_shared < 0 || E + n_shared > MOE_MAX_EXPERTS)
+        return MOE_EINVAL;
+    if (T * (int64_t)(k + n_shared) > kInt32Max || T * (int64_t)E > ((int64_t)1 << 40))
+        return MOE_EINVAL;
+    if (T == 0) return MOE_OK;
+    if (!logits || !topk_idx || !topk_w) return MOE_ENULL;
+    if (!aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4)) return MOE_EALIGN;
+    moe::LaunchInfo info;
+    const hipError_t e = moe::launch_route_topk(logits, T, E, k, n_shared, shared_w, topk_idx,
+                                                topk_w, static_cast<hipStream_t>(stream), &info);
+    if (log_enabled()) log_launch("route_topk_shared", info);
+    return status_of(e);
+}
+
+int moe_route_replicas(int32_t* topk_idx, int64_t T, int k, int E, const int32_t* replica_base,
+                       void* stream) {
+    if (T < 0 || k < 1 || E < 1 || E > MOE_MAX_EXPERTS) return MOE_EINVAL;
+    if (T * (int64_t)k > kInt32Max) return MOE_EINVAL;
+    if (T == 0) return MOE_OK;
+    if (!topk_idx || !replica_base) return MOE_ENULL;
+    if (!aligned(topk_idx, 4) || !aligned(replica_base, 4)) return MOE_EALIGN;
+    return status_of(moe::launch_route_replicas(topk_idx, T, k, E, replica_base,
+                                                static_cast<hipStream_t>(stream)));
 }
 
 int64_t moe_dispatch_max_rows(int64_t T, int E, int k, int row_align) {

@@ -18,9 +18,12 @@ struct LaunchInfo {
     int64_t param = 0;   // kernel-specific: lanes per token, tokens per block, ...
 };
 
-hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k,
-                             int32_t* topk_idx, float* topk_w, hipStream_t stream,
-                             LaunchInfo* info);
+hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k, int n_shared,
+                             float shared_w, int32_t* topk_idx, float* topk_w,
+                             hipStream_t stream, LaunchInfo* info);
+
+hipError_t launch_route_replicas(int32_t* topk_idx, int64_t T, int k, int E,
+                                 const int32_t* replica_base, hipStream_t stream);
 
 struct DispatchArgs {
     const void* x;

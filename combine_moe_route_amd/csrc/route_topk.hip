@@ -72,7 +72,8 @@ constexpr int kRouteThreads = 256;
 
 template <int S, int NV>
 __global__ __launch_bounds__(kRouteThreads) void k_route_topk(const float* __restrict__ logits, int64_t T,
-                                                    int E, int k, int32_t* __restrict__ topk_idx,
+                                                    int E, int k, int ks, int n_shared,
+                                                    float shared_w, int32_t* __restrict__ topk_idx,
                                                     float* __restrict__ topk_w) {
     constexpr uint32_t kNone = 0xFFFFFFFFu;
     const int lane = threadIdx.x & (kWave - 1);
@@ -166,16 +167,20 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_topk(const float* __res
         const float sum = __uint_as_float(group_reduce<S>(__float_as_uint(part), FAdd()));
         if (live) {
             if (lane < k) {
-                topk_idx[t * k + lane] = sel_e;
-                topk_w[t * k + lane] = ex0 / sum;
+                topk_idx[t * ks + lane] = sel_e;
+                topk_w[t * ks + lane] = ex0 / sum;
             }
 #pragma unroll
             for (int i = 1; i < NV; i++) {
                 const int r = lane + kWave * i;
                 if (r < k) {
-                    topk_idx[t * k + r] = hi_e[i];
-                    topk_w[t * k + r] = exh[i] / sum;
+                    topk_idx[t * ks + r] = hi_e[i];
+                    topk_w[t * ks + r] = exh[i] / sum;
                 }
+            }
+            for (int sh = lane; sh < n_shared; sh += kWave) {
+                topk_idx[t * ks + k + sh] = E + sh;
+                topk_w[t * ks + k + sh] = shared_w;
             }
         }
     } else {
@@ -199,22 +204,35 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_topk(const float* __res
         const float ex = g < k ? expf(key_value(sel_key) - key_value(first)) : 0.0f;
         const float sum = __uint_as_float(group_reduce<S>(__float_as_uint(ex), FAdd()));
         if (live && g < k) {
-            topk_idx[t * k + g] = sel_e;
-            topk_w[t * k + g] = ex / sum;
+            topk_idx[t * ks + g] = sel_e;
+            topk_w[t * ks + g] = ex / sum;
         }
+        if (live)
+            for (int sh = g; sh < n_shared; sh += S) {
+                topk_idx[t * ks + k + sh] = E + sh;
+                topk_w[t * ks + k + sh] = shared_w;
+            }
     }
 }
 
+struct RouteArgs {
+    const float* logits;
+    int64_t T;
+    int E, k, ks, n_shared;
+    float shared_w;
+    int32_t* topk_idx;
+    float* topk_w;
+};
+
 template <int S, int NV>
-static void launch_s(const float* logits, int64_t T, int E, int k, int32_t* topk_idx,
-                     float* topk_w, hipStream_t stream, int64_t blocks) {
-    k_route_topk<S, NV><<<dim3((unsigned)blocks), dim3(kRouteThreads), 0, stream>>>(logits, T, E, k, topk_idx,
-                                                                        topk_w);
+static void launch_s(const RouteArgs& a, hipStream_t stream, int64_t blocks) {
+    k_route_topk<S, NV><<<dim3((unsigned)blocks), dim3(kRouteThreads), 0, stream>>>(
+        a.logits, a.T, a.E, a.k, a.ks, a.n_shared, a.shared_w, a.topk_idx, a.topk_w);
 }
 
-hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k,
-                             int32_t* topk_idx, float* topk_w, hipStream_t stream,
-                             LaunchInfo* info) {
+hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k, int n_shared,
+                             float shared_w, int32_t* topk_idx, float* topk_w,
+                             hipStream_t stream, LaunchInfo* info) {
     int S = 1;
     while (S < E && S < kWave) S <<= 1;
     const int nv = (E + S - 1) / S;
@@ -223,20 +241,46 @@ hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k,
     const int64_t blocks = (T + tokens_per_block - 1) / tokens_per_block;
     if (info) *info = LaunchInfo{blocks, threads, 0, S};
     if (blocks == 0) return hipSuccess;
+    const RouteArgs a{logits, T, E, k, k + n_shared, n_shared, shared_w, topk_idx, topk_w};
     switch (S) {
-        case 1: launch_s<1, 1>(logits, T, E, k, topk_idx, topk_w, stream, blocks); break;
-        case 2: launch_s<2, 1>(logits, T, E, k, topk_idx, topk_w, stream, blocks); break;
-        case 4: launch_s<4, 1>(logits, T, E, k, topk_idx, topk_w, stream, blocks); break;
-        case 8: launch_s<8, 1>(logits, T, E, k, topk_idx, topk_w, stream, blocks); break;
-        case 16: launch_s<16, 1>(logits, T, E, k, topk_idx, topk_w, stream, blocks); break;
-        case 32: launch_s<32, 1>(logits, T, E, k, topk_idx, topk_w, stream, blocks); break;
+        case 1: launch_s<1, 1>(a, stream, blocks); break;
+        case 2: launch_s<2, 1>(a, stream, blocks); break;
+        case 4: launch_s<4, 1>(a, stream, blocks); break;
+        case 8: launch_s<8, 1>(a, stream, blocks); break;
+        case 16: launch_s<16, 1>(a, stream, blocks); break;
+        case 32: launch_s<32, 1>(a, stream, blocks); break;
         default:
-            if (nv <= 1) launch_s<64, 1>(logits, T, E, k, topk_idx, topk_w, stream, blocks);
-            else if (nv <= 2) launch_s<64, 2>(logits, T, E, k, topk_idx, topk_w, stream, blocks);
-            else if (nv <= 4) launch_s<64, 4>(logits, T, E, k, topk_idx, topk_w, stream, blocks);
-            else if (nv <= 8) launch_s<64, 8>(logits, T, E, k, topk_idx, topk_w, stream, blocks);
-            else launch_s<64, 16>(logits, T, E, k, topk_idx, topk_w, stream, blocks);
+            if (nv <= 1) launch_s<64, 1>(a, stream, blocks);
+            else if (nv <= 2) launch_s<64, 2>(a, stream, blocks);
+            else if (nv <= 4) launch_s<64, 4>(a, stream, blocks);
+            else if (nv <= 8) launch_s<64, 8>(a, stream, blocks);
+            else launch_s<64, 16>(a, stream, blocks);
     }
+    return hipGetLastError();
+}
+
+// Redundant replicas: logical expert e owns physical experts
+// replica_base[e] .. replica_base[e+1]-1 and token t uses copy t mod count.
+__global__ __launch_bounds__(256) void k_route_replicas(int32_t* __restrict__ topk_idx, int64_t T,
+                                                        int k, int E,
+                                                        const int32_t* __restrict__ replica_base) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= T * k) return;
+    const int e = topk_idx[i];
+    if ((unsigned)e >= (unsigned)E) return;
+    const int b = replica_base[e];
+    const int n = replica_base[e + 1] - b;
+    if (n <= 0) return;
+    topk_idx[i] = b + (int)((i / k) % n);
+}
+
+hipError_t launch_route_replicas(int32_t* topk_idx, int64_t T, int k, int E,
+                                 const int32_t* replica_base, hipStream_t stream) {
+    const int64_t n = T * k;
+    const int64_t blocks = (n + 255) / 256;
+    if (blocks == 0) return hipSuccess;
+    k_route_replicas<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(topk_idx, T, k, E,
+                                                                      replica_base);
     return hipGetLastError();
 }
 

@@ -75,6 +75,32 @@ typedef enum {
 int moe_route_topk(const float* logits, int64_t T, int E, int k,
                    int32_t* topk_idx, float* topk_w, void* stream);
 
+/*
+ * Shared experts treated as routed ones (DeepSeek-V3 excerpt on the third
+ * page: every token selects its routed experts plus the shared expert, a
+ * heavy-load expert that is always chosen). Same as moe_route_topk for slots
+ * 0..k-1; slots k..k+n_shared-1 hold experts E..E+n_shared-1 with weight
+ * shared_w (the pages do not give the shared expert's weight; 1 adds its
+ * output unweighted). Outputs are [T, k + n_shared]; dispatch them with
+ * E + n_shared experts and k + n_shared slots.
+ *   0 <= n_shared, E + n_shared <= MOE_MAX_EXPERTS; other limits as above.
+ */
+int moe_route_topk_shared(const float* logits, int64_t T, int E, int k, int n_shared,
+                          float shared_w, int32_t* topk_idx, float* topk_w, void* stream);
+
+/*
+ * Redundant expert replicas (DeepSeek-V3 excerpts: heavily loaded experts get
+ * extra copies hosted as separate experts). In place on topk_idx [T, k]:
+ * logical expert e owns physical experts replica_base[e] ..
+ * replica_base[e+1]-1 (device int32 [E+1], non-decreasing, each e with at
+ * least one copy) and token t uses copy t mod (its number of copies). Ids
+ * outside [0, E) are left unchanged. Choosing which experts to replicate
+ * (from load statistics) is the caller's; dispatch the result with
+ * replica_base[E] experts.
+ */
+int moe_route_replicas(int32_t* topk_idx, int64_t T, int k, int E,
+                       const int32_t* replica_base, void* stream);
+
 /* Rows dispatch may use: T*k + E*(row_align-1); -1 if the arguments are
  * invalid or the count does not fit in int32. */
 int64_t moe_dispatch_max_rows(int64_t T, int E, int k, int row_align);

@@ -62,6 +62,10 @@ def _load():
     lib.oracle_quantize_block.restype = None
     lib.oracle_combine_sender.argtypes = [P, P, P, P, i64, i32, i32, i32, i32, P, P, P]
     lib.oracle_combine_sender.restype = None
+    lib.oracle_route_topk_shared.argtypes = [P, i64, i32, i32, i32, ctypes.c_float, P, P]
+    lib.oracle_route_topk_shared.restype = None
+    lib.oracle_route_replicas.argtypes = [P, i64, i32, i32, P]
+    lib.oracle_route_replicas.restype = None
     lib.oracle_e4m3_encode_array.argtypes = [P, P, i64]
     lib.oracle_e4m3_encode_array.restype = None
     lib.oracle_e4m3_encode_bits.argtypes = [ctypes.c_uint32, i64, P]
@@ -89,6 +93,26 @@ def route_topk(logits: np.ndarray, k: int):
     w = np.empty((T, k), np.float32)
     _load().oracle_route_topk(_p(logits), T, E, k, _p(idx), _p(w))
     return idx, w
+
+
+def route_topk_shared(logits: np.ndarray, k: int, n_shared: int, shared_w: float = 1.0):
+    """Routed top-k plus n_shared always-chosen experts E..E+n_shared-1."""
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    idx = np.empty((T, k + n_shared), np.int32)
+    w = np.empty((T, k + n_shared), np.float32)
+    _load().oracle_route_topk_shared(_p(logits), T, E, k, n_shared, shared_w, _p(idx), _p(w))
+    return idx, w
+
+
+def route_replicas(topk_idx: np.ndarray, E: int, replica_base: np.ndarray) -> np.ndarray:
+    """Logical expert ids -> physical replica ids (copy t mod count)."""
+    idx = np.array(topk_idx, dtype=np.int32, copy=True, order="C")
+    T, k = idx.shape
+    base = _c(replica_base, np.int32)
+    assert base.shape == (E + 1,)
+    _load().oracle_route_replicas(_p(idx), T, k, E, _p(base))
+    return idx
 
 
 class Dispatch(NamedTuple):

@@ -370,3 +370,45 @@ void oracle_combine_sender(const uint16_t* expert_out, const int32_t* dst_row,
     free(acc);
     free(tot);
 }
+
+/* ---------------------------------------------------------------- routing variants */
+
+/* Shared experts treated as routed ones (DeepSeek-V3 excerpt on the third
+ * page: each token selects 8 routed experts plus the shared expert, which is
+ * always chosen). Slots 0..k-1 are the routed top-k of oracle_route_topk;
+ * slots k..k+n_shared-1 hold experts E..E+n_shared-1 with weight shared_w.
+ * Row stride of the outputs is k + n_shared. */
+void oracle_route_topk_shared(const float* logits, int64_t T, int E, int k, int n_shared,
+                              float shared_w, int32_t* topk_idx, float* topk_w) {
+    const int ks = k + n_shared;
+    int32_t* idx = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+    float* w = (float*)malloc(sizeof(float) * (size_t)k);
+    for (int64_t t = 0; t < T; t++) {
+        oracle_route_topk(logits + t * (int64_t)E, 1, E, k, idx, w);
+        for (int j = 0; j < k; j++) {
+            topk_idx[t * ks + j] = idx[j];
+            topk_w[t * ks + j] = w[j];
+        }
+        for (int s = 0; s < n_shared; s++) {
+            topk_idx[t * ks + k + s] = E + s;
+            topk_w[t * ks + k + s] = shared_w;
+        }
+    }
+    free(idx);
+    free(w);
+}
+
+/* Redundant replicas (DeepSeek-V3 excerpts: experts with heavy load get extra
+ * copies hosted as separate experts). Logical expert e owns the physical
+ * experts replica_base[e] .. replica_base[e+1]-1; token t goes to copy
+ * t mod (number of copies). Ids outside [0, E) pass through unchanged. */
+void oracle_route_replicas(int32_t* topk_idx, int64_t T, int k, int E,
+                           const int32_t* replica_base) {
+    for (int64_t t = 0; t < T; t++)
+        for (int j = 0; j < k; j++) {
+            int e = topk_idx[t * k + j];
+            if (e < 0 || e >= E) continue;
+            int n = replica_base[e + 1] - replica_base[e];
+            topk_idx[t * k + j] = replica_base[e] + (int)(t % n);
+        }
+}

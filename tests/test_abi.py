@@ -80,6 +80,23 @@ def test_route_topk_validation():
     assert route(T=0, logits=None, idx=None, w=None) == OK      # no-op
 
 
+def test_route_variant_validation():
+    sh = lambda logits=A, T=16, E=8, k=2, ns=1, idx=B, w=B + 4096: lib.moe_route_topk_shared(
+        logits, T, E, k, ns, 1.0, idx, w, None)
+    assert sh(ns=-1) == EINVAL
+    assert sh(E=1020, ns=5) == EINVAL                   # E + n_shared > 1024
+    assert sh(k=9) == EINVAL
+    assert sh(logits=None) == ENULL
+    assert sh(w=B + 2) == EALIGN
+    assert sh(T=0, logits=None, idx=None, w=None) == OK
+    rep = lambda idx=B, T=16, k=2, E=8, base=A: lib.moe_route_replicas(idx, T, k, E, base, None)
+    assert rep(E=0) == EINVAL
+    assert rep(k=0) == EINVAL
+    assert rep(base=None) == ENULL
+    assert rep(idx=B + 1) == EALIGN
+    assert rep(T=0, idx=None, base=None) == OK
+
+
 def dispatch(**kw):
     a = dict(x=A, idx=B, T=256, H=256, E=8, k=2, groups=1, row_align=1, dt=0, out=A + 2 ** 20,
              scales=A + 2 ** 21, counts=B + 2 ** 20, offsets=B + 2 ** 20 + 64,

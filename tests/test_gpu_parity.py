@@ -327,3 +327,40 @@ def test_combine_sender_side(dev, c, G):
     send = bf16_bits_to_f32(y_ref).astype(np.float64)
     log(f"  mean |error|: receiver-only {np.mean(np.abs(recv - exact_sum)):.3e}, "
         f"sender-side {np.mean(np.abs(send - exact_sum)):.3e}")
+
+
+@pytest.mark.parametrize("E,k,n_shared,sw", [(8, 2, 1, 1.0), (256, 8, 1, 1.0), (384, 8, 2, 0.5),
+                                             (16, 16, 3, 1.0), (100, 7, 64, 2.0)])
+def test_route_shared_experts(dev, E, k, n_shared, sw):
+    """Shared experts as always-chosen slots, then the full chain with E + n_shared experts."""
+    from combine_moe_route_amd import moe_route_topk_shared
+    T = 300
+    l = gen_logits(T, E, seed=E + n_shared)
+    ri, rw = oracle.route_topk_shared(l, k, n_shared, sw)
+    gi, gw = moe_route_topk_shared(torch.from_numpy(l).to(dev), k, n_shared, sw)
+    torch.cuda.synchronize()
+    assert np.array_equal(gi.cpu().numpy(), ri)
+    gw = gw.cpu().numpy()
+    assert np.all(np.abs(gw - rw) <= 1e-5 * np.abs(rw))
+    assert np.all(gw[:, k:] == np.float32(sw))
+    if E + n_shared <= 1024:
+        full_case(Case(T=T, H=256, E=E + n_shared, k=k + n_shared, groups=1, row_align=4,
+                       seed=E), dev, idx_np=ri)
+
+
+def test_route_replicas(dev):
+    from combine_moe_route_amd import moe_route_replicas
+    rng = np.random.default_rng(61)
+    E, T, k = 64, 1000, 6
+    copies = rng.integers(1, 5, E)
+    base = np.concatenate([[0], np.cumsum(copies)]).astype(np.int32)
+    idx, w = oracle.route_topk(gen_logits(T, E, seed=61, zipf_s=1.1), k)
+    idx[::13, 2] = -1
+    want = oracle.route_replicas(idx, E, base)
+    g = torch.from_numpy(idx.copy()).to(dev)
+    moe_route_replicas(g, E, torch.from_numpy(base).to(dev))
+    torch.cuda.synchronize()
+    assert np.array_equal(g.cpu().numpy(), want)
+    # the chain on physical experts
+    full_case(Case(T=T, H=512, E=int(base[-1]), k=k, groups=1, row_align=8, fp8=True, seed=62),
+              dev, idx_np=want)

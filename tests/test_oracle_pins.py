@@ -647,3 +647,40 @@ def test_sender_receiver_half_sums_the_rounded_partials():
     err = np.abs(got - s)
     ok = ((err <= np.abs(up - s)) & (err <= np.abs(dn - s))) | ((y & 0x7FFF) == 0)
     assert ok.all()
+
+
+# ----------------------------------------------------------------- routing variants
+
+def test_route_shared_experts_extend_the_routed_slots():
+    l = gen_logits(120, 64, seed=51)
+    for n_shared, sw in [(1, 1.0), (2, 0.5)]:
+        idx, w = oracle.route_topk_shared(l, 8, n_shared, sw)
+        ri, rw = oracle.route_topk(l, 8)
+        assert np.array_equal(idx[:, :8], ri) and np.array_equal(w[:, :8], rw)
+        assert np.all(idx[:, 8:] == 64 + np.arange(n_shared)) and np.all(w[:, 8:] == np.float32(sw))
+        # dispatch puts every token into each shared expert's segment, in token order
+        x = gen_x_bf16(120, 64, seed=51)
+        d = oracle.dispatch(x, idx, 64 + n_shared)
+        for s in range(n_shared):
+            seg = d.row_src[d.expert_offsets[64 + s]:d.expert_offsets[65 + s]]
+            assert np.array_equal(seg, np.arange(120) * (8 + n_shared) + 8 + s)
+
+
+def test_route_replicas_map_back_and_spread():
+    rng = np.random.default_rng(52)
+    E, T, k = 16, 500, 4
+    copies = rng.integers(1, 4, E)
+    base = np.concatenate([[0], np.cumsum(copies)]).astype(np.int32)
+    idx, _ = oracle.route_topk(gen_logits(T, E, seed=52), k)
+    idx[::11, 0] = -1
+    phys = oracle.route_replicas(idx, E, base)
+    live = idx >= 0
+    # each physical id maps back to its logical expert (library search)
+    back = np.searchsorted(base, phys[live], side="right") - 1
+    assert np.array_equal(back, idx[live])
+    assert np.array_equal(phys[~live], idx[~live])
+    # the copy used by token t is t mod copies
+    t_of = np.broadcast_to(np.arange(T)[:, None], idx.shape)[live]
+    assert np.array_equal(phys[live] - base[idx[live]], t_of % copies[idx[live]])
+    # one copy everywhere is the identity
+    assert np.array_equal(oracle.route_replicas(idx, E, np.arange(E + 1, dtype=np.int32)), idx)
