@@ -193,6 +193,106 @@ def run_sender(w, steps, cold, scratch, stream, expert_out, bufs, topk_idx, topk
                 mean_abs_err=err_send, mean_abs_err_receiver_only=err_recv)
 
 
+def time_steps(step, steps, warmup, cold, scratch, stream):
+    """Median of `steps` event-timed calls of step() (cache flushed before each)."""
+    import torch
+    for _ in range(warmup):
+        if cold:
+            scratch.fill_(1)
+        step()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        if cold:
+            scratch.fill_(1)
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return statistics.median([a.elapsed_time(b) * 1e3 for a, b in ev])
+
+
+def run_routing_variants(steps, warmup, cold=True):
+    """Shared expert on the 16384-token FP8 workload; load-proportional
+    replicas on the skewed 4096-token workload."""
+    import torch
+
+    from combine_moe_route_amd import (alloc_dispatch, moe_combine, moe_dispatch,
+                                       moe_dispatch_max_rows, moe_harness_expert_scale,
+                                       moe_route_replicas, moe_route_topk, moe_route_topk_shared)
+    from moe_synth import WORKLOADS, gen_inputs
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    res = {}
+
+    # (a) one shared expert, always chosen, weight 1
+    w = WORKLOADS["dsv3_prefill"]
+    x_np, l_np = gen_inputs(w)
+    x = torch.from_numpy(x_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    logits = torch.from_numpy(l_np).to(dev)
+    E2, k2 = w.E + 1, w.k + 1
+    idx = torch.empty((w.T, k2), dtype=torch.int32, device=dev)
+    wt = torch.empty((w.T, k2), dtype=torch.float32, device=dev)
+    bufs = alloc_dispatch(w.T, w.H, E2, k2, 1, w.row_align, w.fp8, dev)
+    eo = torch.empty((moe_dispatch_max_rows(w.T, E2, k2, w.row_align), w.H), dtype=torch.bfloat16,
+                     device=dev)
+    y = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev)
+    moe_route_topk_shared(logits, w.k, 1, 1.0, idx, wt)
+    moe_dispatch(x, idx, E2, 1, w.row_align, w.fp8, bufs)
+    moe_harness_expert_scale(bufs, idx, E2, w.fp8, expert_out=eo)
+    torch.cuda.synchronize()
+    R = int(bufs.expert_offsets[-1].item())
+
+    def step_shared():
+        moe_route_topk_shared(logits, w.k, 1, 1.0, idx, wt)
+        moe_dispatch(x, idx, E2, 1, w.row_align, w.fp8, bufs)
+        moe_combine(eo, bufs.dst_row, wt, y)
+    us = time_steps(step_shared, steps, warmup, cold, scratch, stream)
+    bd, bc = algorithmic_bytes(w.T, w.H, E2, k2, R, w.fp8)
+    res["shared_expert"] = dict(workload=w.name, experts=E2, slots=k2, rows=R, us_total=round(us, 2),
+                                gbps=round((bd + bc) / (us * 1e-6) / 1e9, 1),
+                                pct_of_peak=round(100 * (bd + bc) / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 2))
+    del bufs, eo, x, logits, idx, wt, y
+
+    # (b) replicas proportional to the observed load of each expert
+    w = WORKLOADS["kimi_prefill"]
+    x_np, l_np = gen_inputs(w)
+    x = torch.from_numpy(x_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    logits = torch.from_numpy(l_np).to(dev)
+    idx = torch.empty((w.T, w.k), dtype=torch.int32, device=dev)
+    wt = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
+    moe_route_topk(logits, w.k, idx, wt)
+    b0 = moe_dispatch(x, idx, w.E, 1, w.row_align, w.fp8)
+    counts = b0.expert_counts.cpu().numpy().astype(np.int64)
+    mean = w.T * w.k / w.E
+    copies = np.maximum(1, np.ceil(counts / mean)).astype(np.int64)
+    base = torch.from_numpy(np.concatenate([[0], np.cumsum(copies)]).astype(np.int32)).to(dev)
+    Ep = int(copies.sum())
+    bufs = alloc_dispatch(w.T, w.H, Ep, w.k, 1, w.row_align, w.fp8, dev)
+    eo = torch.empty((moe_dispatch_max_rows(w.T, Ep, w.k, w.row_align), w.H), dtype=torch.bfloat16,
+                     device=dev)
+    y = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev)
+    moe_route_replicas(idx, w.E, base)
+    moe_dispatch(x, idx, Ep, 1, w.row_align, w.fp8, bufs)
+    moe_harness_expert_scale(bufs, idx, Ep, w.fp8, expert_out=eo)
+    torch.cuda.synchronize()
+    max_after = int(bufs.expert_counts.max().item())
+
+    def step_rep():
+        moe_route_topk(logits, w.k, idx, wt)
+        moe_route_replicas(idx, w.E, base)
+        moe_dispatch(x, idx, Ep, 1, w.row_align, w.fp8, bufs)
+        moe_combine(eo, bufs.dst_row, wt, y)
+    us = time_steps(step_rep, steps, warmup, cold, scratch, stream)
+    bd, bc = algorithmic_bytes(w.T, w.H, Ep, w.k, w.T * w.k, w.fp8)
+    res["replicas"] = dict(workload=w.name, logical_experts=w.E, physical_experts=Ep,
+                           max_rows_per_expert_before=int(counts.max()),
+                           max_rows_per_expert_after=max_after, us_total=round(us, 2),
+                           gbps=round((bd + bc) / (us * 1e-6) / 1e9, 1))
+    return res
+
+
 def copy_bandwidth(nbytes=1 << 30, reps=10):
     """Device-to-device copy bandwidth (read + write bytes / time)."""
     import torch
@@ -263,6 +363,8 @@ def main():
                     help="comma-separated extra workloads reported under 'other' ('' for none)")
     ap.add_argument("--warm", action="store_true", help="skip the cache flush between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the routing-variant measurements reported under 'next'")
     ap.add_argument("--cpu-tokens", type=int, default=16384)
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run 1 GiB device copies (counter calibration)")
@@ -331,6 +433,9 @@ def main():
         "other": others,
         "next": {"sender_side_combine": r.get("sender")},
     }
+    if not args.no_variants:
+        print("[bench] routing variants", file=sys.stderr, flush=True)
+        out["next"].update(run_routing_variants(args.steps, args.warmup, cold=not args.warm))
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens)
