@@ -293,6 +293,119 @@ def run_routing_variants(steps, warmup, cold=True):
     return res
 
 
+def cu_budget(w, steps):
+    """Dispatch + combine restricted to N CUs through CU-masked streams, and
+    the same steps overlapped with a bf16 GEMM confined to the other CUs."""
+    import ctypes
+
+    import torch
+
+    from combine_moe_route_amd import (alloc_dispatch, moe_combine, moe_dispatch,
+                                       moe_dispatch_max_rows, moe_harness_expert_scale,
+                                       moe_route_topk)
+    from moe_synth import gen_inputs
+    hip = ctypes.CDLL("libamdhip64.so")
+    dev = torch.device("cuda:0")
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    made = []
+
+    def masked(cus):
+        mask = (ctypes.c_uint32 * ((n_cu + 31) // 32))()
+        for c in cus:
+            mask[c // 32] |= 1 << (c % 32)
+        h = ctypes.c_void_p()
+        err = hip.hipExtStreamCreateWithCUMask(ctypes.byref(h), len(mask), mask)
+        if err != 0:
+            raise RuntimeError(f"hipExtStreamCreateWithCUMask failed: {err}")
+        made.append(h)
+        return torch.cuda.ExternalStream(h.value, device=dev)
+
+    x_np, l_np = gen_inputs(w)
+    x = torch.from_numpy(x_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    logits = torch.from_numpy(l_np).to(dev)
+    idx = torch.empty((w.T, w.k), dtype=torch.int32, device=dev)
+    wt = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
+    bufs = alloc_dispatch(w.T, w.H, w.E, w.k, w.groups, w.row_align, w.fp8, dev)
+    eo = torch.empty((moe_dispatch_max_rows(w.T, w.E, w.k, w.row_align), w.H), dtype=torch.bfloat16,
+                     device=dev)
+    y = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev)
+    moe_route_topk(logits, w.k, idx, wt)
+    moe_dispatch(x, idx, w.E, w.groups, w.row_align, w.fp8, bufs)
+    moe_harness_expert_scale(bufs, idx, w.E, w.fp8, expert_out=eo)
+    gen = torch.Generator(device=dev).manual_seed(0)
+    ga = torch.randn((8192, 8192), dtype=torch.bfloat16, device=dev, generator=gen)
+    gb = torch.randn((8192, 8192), dtype=torch.bfloat16, device=dev, generator=gen)
+    gc = torch.empty((8192, 8192), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    def moe_step():
+        moe_route_topk(logits, w.k, idx, wt)
+        moe_dispatch(x, idx, w.E, w.groups, w.row_align, w.fp8, bufs)
+        moe_combine(eo, bufs.dst_row, wt, y)
+
+    def gemm():
+        torch.matmul(ga, gb, out=gc)
+
+    def timed(fn, reps, stream):
+        with torch.cuda.stream(stream):
+            fn()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / reps
+
+    full = torch.cuda.current_stream(dev)
+    t_moe_full = timed(moe_step, steps, full)
+    t_gemm_full = timed(gemm, steps, full)
+    gemm_reps = max(1, round(steps * t_moe_full / t_gemm_full))
+    rows = []
+    for n in (32, 64, 128, 192, 256):
+        # consecutive mask bits are spread over the XCDs (a mask that leaves an
+        # XCD without CUs is rejected), so [0, n) is an even n-CU budget
+        cus = list(range(min(n, n_cu)))
+        rest = list(range(min(n, n_cu), n_cu))
+        print(f"[bench] cu budget {n}", file=sys.stderr, flush=True)
+        s_moe = masked(cus)
+        t_moe = timed(moe_step, steps, s_moe)
+        row = dict(cus=n, us_moe_step=round(t_moe, 1))
+        if rest:
+            s_rest = masked(rest)
+            t_gemm = timed(gemm, gemm_reps, s_rest)
+            # overlap: both streams start after one marker, run concurrently
+            start = torch.cuda.Event()
+            start.record(full)
+            s_moe.wait_event(start)
+            s_rest.wait_event(start)
+            e_m, e_g = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e0.record(full)
+            with torch.cuda.stream(s_moe):
+                for _ in range(steps):
+                    moe_step()
+                e_m.record(s_moe)
+            with torch.cuda.stream(s_rest):
+                for _ in range(gemm_reps):
+                    gemm()
+                e_g.record(s_rest)
+            torch.cuda.synchronize()
+            makespan = max(e0.elapsed_time(e_m), e0.elapsed_time(e_g)) * 1e3
+            seq = steps * t_moe_full + gemm_reps * t_gemm_full
+            row.update(us_gemm_on_rest=round(t_gemm, 1), us_moe_steps_end=round(e0.elapsed_time(e_m) * 1e3, 1),
+                       us_gemms_end=round(e0.elapsed_time(e_g) * 1e3, 1),
+                       us_makespan=round(makespan, 1), us_sequential_full_gpu=round(seq, 1),
+                       overlap_speedup=round(seq / makespan, 3))
+        rows.append(row)
+        torch.cuda.synchronize()
+        while made:
+            hip.hipStreamDestroy(made.pop())
+    return dict(workload=w.name, moe_steps=steps, gemm="bf16 8192x8192x8192", gemm_reps=gemm_reps,
+                us_moe_step_full_gpu=round(t_moe_full, 1), us_gemm_full_gpu=round(t_gemm_full, 1),
+                budgets=rows)
+
+
 def copy_bandwidth(nbytes=1 << 30, reps=10):
     """Device-to-device copy bandwidth (read + write bytes / time)."""
     import torch
@@ -366,6 +479,8 @@ def main():
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the routing-variant measurements reported under 'next'")
     ap.add_argument("--cpu-tokens", type=int, default=16384)
+    ap.add_argument("--cu-budget", action="store_true",
+                    help="only run the CU-budget / overlap experiment")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run 1 GiB device copies (counter calibration)")
     args = ap.parse_args()
@@ -379,6 +494,10 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     from moe_synth import WORKLOADS
+
+    if args.cu_budget:
+        print(json.dumps({"cu_budget": cu_budget(WORKLOADS[args.workload], args.steps)}), flush=True)
+        return
 
     if args.calib_copy:
         print(json.dumps({"copy_GBps": round(copy_bandwidth(), 1), "bytes_per_copy": 1 << 30}),
