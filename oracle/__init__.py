@@ -70,6 +70,12 @@ def _load():
     lib.oracle_e4m3_encode_array.restype = None
     lib.oracle_e4m3_encode_bits.argtypes = [ctypes.c_uint32, i64, P]
     lib.oracle_e4m3_encode_bits.restype = None
+    lib.oracle_quantize_weights.argtypes = [P, i64, i64, P, P]
+    lib.oracle_quantize_weights.restype = None
+    lib.oracle_grouped_gemm_fp8.argtypes = [P, P, P, i32, P, P, i32, i32, P, P, P]
+    lib.oracle_grouped_gemm_fp8.restype = None
+    lib.oracle_grouped_gemm_fp8_at.argtypes = [P, P, P, i32, P, P, i32, i32, P, P, i64, P, P, P]
+    lib.oracle_grouped_gemm_fp8_at.restype = None
     _lib = lib
     return lib
 
@@ -231,3 +237,68 @@ def quantize_block(xblock: np.ndarray):
     s = np.empty(1, np.float32)
     _load().oracle_quantize_block(_p(xb), _p(q), _p(s))
     return q, s[0]
+
+
+def quantize_weights(w: np.ndarray):
+    """128x128-block E4M3 quantisation of fp32 weights [..., N, K]:
+    (codes uint8 [..., N, K], scales float32 [..., N/128, K/128])."""
+    w = _c(w, np.float32)
+    N, K = w.shape[-2:]
+    assert N % 128 == 0 and K % 128 == 0
+    lead = w.shape[:-2]
+    wf = w.reshape(-1, N, K)
+    q = np.empty(wf.shape, np.uint8)
+    s = np.empty((wf.shape[0], N // 128, K // 128), np.float32)
+    for i in range(wf.shape[0]):
+        _load().oracle_quantize_weights(_p(wf[i]), N, K, _p(q[i]), _p(s[i]))
+    return q.reshape(w.shape), s.reshape(lead + (N // 128, K // 128))
+
+
+class Gemm(NamedTuple):
+    y: np.ndarray        # uint16 bf16 bits
+    y64: np.ndarray      # float64 exact-order sum
+    mag: np.ndarray      # float64 sum of absolute terms
+
+
+def grouped_gemm_fp8(a: np.ndarray, a_scales: np.ndarray, expert_offsets: np.ndarray,
+                     w: np.ndarray, w_scales: np.ndarray) -> Gemm:
+    """Block-scaled FP8 grouped GEMM over the padded segments. Rows at or
+    past expert_offsets[E] are returned as zero."""
+    a = _c(a, np.uint8)
+    a_scales = _c(a_scales, np.float32)
+    off = _c(expert_offsets, np.int32)
+    w = _c(w, np.uint8)
+    w_scales = _c(w_scales, np.float32)
+    E, N, K = w.shape
+    assert off.shape == (E + 1,) and a.shape[1] == K and a_scales.shape == (a.shape[0], K // 128)
+    assert w_scales.shape == (E, N // 128, K // 128) and int(off[E]) <= a.shape[0]
+    rows = a.shape[0]
+    y = np.zeros((rows, N), np.uint16)
+    y64 = np.zeros((rows, N), np.float64)
+    mag = np.zeros((rows, N), np.float64)
+    _load().oracle_grouped_gemm_fp8(_p(a), _p(a_scales), _p(off), E, _p(w), _p(w_scales), N, K,
+                                    _p(y), _p(y64), _p(mag))
+    return Gemm(y, y64, mag)
+
+
+def grouped_gemm_fp8_at(a: np.ndarray, a_scales: np.ndarray, expert_offsets: np.ndarray,
+                        w: np.ndarray, w_scales: np.ndarray, rows: np.ndarray,
+                        cols: np.ndarray) -> Gemm:
+    """The grouped GEMM at chosen (row, column) positions only; every row
+    must lie below expert_offsets[E]."""
+    a = _c(a, np.uint8)
+    a_scales = _c(a_scales, np.float32)
+    off = _c(expert_offsets, np.int32)
+    w = _c(w, np.uint8)
+    w_scales = _c(w_scales, np.float32)
+    E, N, K = w.shape
+    rows = _c(rows, np.int64)
+    cols = _c(cols, np.int32)
+    assert rows.shape == cols.shape and (rows < int(off[E])).all() and (cols < N).all()
+    n = rows.size
+    y = np.zeros(n, np.uint16)
+    y64 = np.zeros(n, np.float64)
+    mag = np.zeros(n, np.float64)
+    _load().oracle_grouped_gemm_fp8_at(_p(a), _p(a_scales), _p(off), E, _p(w), _p(w_scales), N, K,
+                                       _p(rows), _p(cols), n, _p(y), _p(y64), _p(mag))
+    return Gemm(y, y64, mag)

@@ -412,3 +412,105 @@ void oracle_route_replicas(int32_t* topk_idx, int64_t T, int k, int E,
             topk_idx[t * k + j] = replica_base[e] + (int)(t % n);
         }
 }
+
+/* ---------------------------------------------------------------- grouped GEMM consumer */
+
+/* Weight quantisation ([DSV3] fine-grained quantisation: weights are grouped
+ * and scaled per 128x128 block, i.e. per 128 output channels per 128 input
+ * channels). w is fp32 [N, K] row-major (K contiguous), N and K multiples of
+ * 128. For block (nb, kb): s = amax / 448 (fp32 division, the same reading as
+ * the 1x128 activation blocks), every element is E4M3(w / s); an all-zero
+ * block has s = 0 and codes 0x00. Scales are [N/128, K/128] row-major. */
+void oracle_quantize_weights(const float* w, int64_t N, int64_t K, uint8_t* q, float* s) {
+    const int64_t KB = K / 128;
+    for (int64_t nb = 0; nb < N / 128; nb++)
+        for (int64_t kb = 0; kb < KB; kb++) {
+            float amax = 0.0f;
+            for (int64_t n = nb * 128; n < nb * 128 + 128; n++)
+                for (int64_t k = kb * 128; k < kb * 128 + 128; k++)
+                    amax = fmaxf(amax, fabsf(w[n * K + k]));
+            const float sc = amax / 448.0f;
+            s[nb * KB + kb] = sc;
+            for (int64_t n = nb * 128; n < nb * 128 + 128; n++)
+                for (int64_t k = kb * 128; k < kb * 128 + 128; k++)
+                    q[n * K + k] = amax == 0.0f ? 0 : oracle_e4m3_encode(w[n * K + k] / sc);
+        }
+}
+
+/* One output of the grouped GEMM. Row r belongs to expert e. Following the
+ * [DSV3] description of FP8 GEMM with fine-grained scales: the product is
+ * summed over each 128-element interval of the inner dimension, that partial
+ * is multiplied by the row's activation scale for the interval and the weight
+ * block's scale, and the result is added to the accumulator. Here every step
+ * is in fp64: products of two E4M3 values are exact, the sums round once per
+ * addition. mag is the same sum over absolute values (the size against which
+ * rounding of the sum is measured). */
+static void gemm_entry(const uint8_t* a, const float* a_scales, const uint8_t* w,
+                       const float* w_scales, int N, int K, int e, int64_t r, int n,
+                       double* val, double* mag) {
+    const int KB = K / 128;
+    const uint8_t* ar = a + r * (int64_t)K;
+    const uint8_t* wn = w + ((int64_t)e * N + n) * (int64_t)K;
+    const float* wsc = w_scales + ((int64_t)e * (N / 128) + n / 128) * KB;
+    double acc = 0.0, accabs = 0.0;
+    for (int b = 0; b < KB; b++) {
+        double part = 0.0, partabs = 0.0;
+        for (int k = b * 128; k < b * 128 + 128; k++) {
+            const double p = (double)oracle_e4m3_value(ar[k]) * (double)oracle_e4m3_value(wn[k]);
+            part += p;
+            partabs += fabs(p);
+        }
+        const double f = (double)a_scales[r * KB + b] * (double)wsc[b];
+        acc += f * part;
+        accabs += fabs(f) * partabs;
+    }
+    *val = acc;
+    *mag = accabs;
+}
+
+/* Expert of a row: the e with off[e] <= r < off[e+1]; -1 past off[E]. */
+static int row_expert(const int32_t* off, int E, int64_t r) {
+    for (int e = 0; e < E; e++)
+        if (r >= off[e] && r < off[e + 1]) return e;
+    return -1;
+}
+
+/* Grouped GEMM over the segments moe dispatch lays out (expert e owns rows
+ * [off[e], off[e+1]) of a, pad rows included):
+ *   y[r, n] = bf16( sum_b a_s[r,b] w_s[e, n/128, b] sum_{k in b} a[r,k] w[e,n,k] )
+ * a: E4M3 [rows, K], a_scales fp32 [rows, K/128], w: E4M3 [E, N, K] (K
+ * contiguous), w_scales fp32 [E, N/128, K/128]. y64 and mag (may be NULL)
+ * receive the fp64 sum and its absolute-value sum. Rows at or past off[E] are
+ * not written. */
+void oracle_grouped_gemm_fp8(const uint8_t* a, const float* a_scales, const int32_t* off, int E,
+                             const uint8_t* w, const float* w_scales, int N, int K,
+                             uint16_t* y, double* y64, double* mag) {
+    for (int64_t r = 0; r < off[E]; r++) {
+        const int e = row_expert(off, E, r);
+        if (e < 0) continue; /* off[0] > 0: rows before the first segment */
+        for (int n = 0; n < N; n++) {
+            double v, m;
+            gemm_entry(a, a_scales, w, w_scales, N, K, e, r, n, &v, &m);
+            y[r * N + n] = oracle_bf16_from_double(v);
+            if (y64) y64[r * N + n] = v;
+            if (mag) mag[r * N + n] = m;
+        }
+    }
+}
+
+/* The same outputs at count chosen (row, column) positions; rows must lie
+ * below off[E]. Outputs are [count]. */
+void oracle_grouped_gemm_fp8_at(const uint8_t* a, const float* a_scales, const int32_t* off, int E,
+                                const uint8_t* w, const float* w_scales, int N, int K,
+                                const int64_t* rows, const int32_t* cols, int64_t count,
+                                uint16_t* y, double* y64, double* mag) {
+    for (int64_t i = 0; i < count; i++) {
+        const int e = row_expert(off, E, rows[i]);
+        double v = 0.0, m = 0.0;
+        if (e >= 0)
+            gemm_entry(a, a_scales, w, w_scales, N, K, e, rows[i], cols[i], &v, &m);
+        y[i] = oracle_bf16_from_double(v);
+        if (y64) y64[i] = v;
+        if (mag) mag[i] = m;
+    }
+}
