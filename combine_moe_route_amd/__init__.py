@@ -19,6 +19,8 @@ _API = (
     "moe_dispatch",
     "moe_dispatch_max_rows",
     "moe_dispatch_workspace_bytes",
+    "moe_grouped_gemm_fp8",
+    "moe_grouped_gemm_workspace_bytes",
     "moe_harness_expert_scale",
     "moe_route_replicas",
     "moe_route_topk",

@@ -33,6 +33,8 @@ EXPORTS = (
     "moe_combine",
     "moe_combine_send",
     "moe_combine_recv",
+    "moe_grouped_gemm_workspace_bytes",
+    "moe_grouped_gemm_fp8",
     "moe_harness_expert_scale",
     "moe_status_string",
 )
@@ -70,6 +72,11 @@ def _load() -> ctypes.CDLL:
     lib.moe_combine_send.restype = i32
     lib.moe_combine_recv.argtypes = [P, P, i64, i32, i32, P, P]
     lib.moe_combine_recv.restype = i32
+    lib.moe_grouped_gemm_workspace_bytes.argtypes = [i64, i32]
+    lib.moe_grouped_gemm_workspace_bytes.restype = ctypes.c_size_t
+    lib.moe_grouped_gemm_fp8.argtypes = [P, P, P, P, P, i32, i32, i32, i64, P, P,
+                                         ctypes.c_size_t, P]
+    lib.moe_grouped_gemm_fp8.restype = i32
     lib.moe_harness_expert_scale.argtypes = [P, P, P, P, P, i64, i32, i32, i32, i32, P, P]
     lib.moe_harness_expert_scale.restype = i32
     lib.moe_status_string.argtypes = [i32]
@@ -311,3 +318,40 @@ def moe_harness_expert_scale(bufs: DispatchBuffers, topk_idx: torch.Tensor, E: i
         MOE_OUT_FP8_E4M3 if fp8 else MOE_OUT_BF16, int(identity), _ptr(expert_out),
         _stream(dev)))
     return expert_out
+
+
+# ----------------------------------------------------------------- grouped GEMM
+
+def moe_grouped_gemm_workspace_bytes(max_rows: int, E: int) -> int:
+    return int(lib.moe_grouped_gemm_workspace_bytes(max_rows, E))
+
+
+def moe_grouped_gemm_fp8(a: torch.Tensor, a_scales: torch.Tensor, expert_offsets: torch.Tensor,
+                         w: torch.Tensor, w_scales: torch.Tensor,
+                         y: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Block-scaled FP8 grouped GEMM over the dispatch segments: y bf16
+    [max_rows, N]; rows at or past expert_offsets[E] are left as they were.
+    a: uint8 E4M3 codes [max_rows, K], a_scales fp32 [max_rows, K/128],
+    w: uint8 E4M3 codes [E, N, K], w_scales fp32 [E, N/128, K/128]."""
+    _need(a, "a", torch.uint8)
+    dev = a.device
+    R, K = a.shape
+    _need(a_scales, "a_scales", torch.float32, (R, K // 128), dev)
+    _need(w, "w", torch.uint8, None, dev)
+    E, N, Kw = w.shape
+    if Kw != K:
+        raise ValueError(f"w: inner size {Kw}, expected {K}")
+    _need(w_scales, "w_scales", torch.float32, (E, N // 128, K // 128), dev)
+    _need(expert_offsets, "expert_offsets", torch.int32, (E + 1,), dev)
+    if y is None:
+        y = torch.empty((R, N), dtype=torch.bfloat16, device=dev)
+    _need(y, "y", torch.bfloat16, (R, N), dev)
+    ws_bytes = moe_grouped_gemm_workspace_bytes(R, E)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, None, dev)
+    _check("moe_grouped_gemm_fp8", lib.moe_grouped_gemm_fp8(
+        _ptr(a), _ptr(a_scales), _ptr(expert_offsets), _ptr(w), _ptr(w_scales), E, N, K, R,
+        _ptr(y), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return y

@@ -11,7 +11,8 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoeroute.so")
-SOURCES = ["api.hip", "route_topk.hip", "dispatch.hip", "combine.hip", "combine_sender.hip"]
+SOURCES = ["api.hip", "route_topk.hip", "dispatch.hip", "combine.hip", "combine_sender.hip",
+           "grouped_gemm.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

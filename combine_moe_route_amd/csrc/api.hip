@@ -236,6 +236,38 @@ int moe_harness_expert_scale(const void* disp, const float* disp_scales, const i
                                               static_cast<hipStream_t>(stream)));
 }
 
+size_t moe_grouped_gemm_workspace_bytes(int64_t max_rows, int E) {
+    if (max_rows < 0 || max_rows > kInt32Max || E < 1 || E > MOE_MAX_EXPERTS) return 0;
+    return moe::gemm_workspace_bytes(max_rows, E);
+}
+
+int moe_grouped_gemm_fp8(const void* a, const float* a_scales, const int32_t* expert_offsets,
+                         const void* w, const float* w_scales, int E, int N, int K,
+                         int64_t max_rows, void* y, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+    if (E < 1 || E > MOE_MAX_EXPERTS || max_rows < 0 || max_rows > kInt32Max) return MOE_EINVAL;
+    if (N < 256 || N > (1 << 20) || N % 256 != 0) return MOE_EINVAL;
+    if (K < 128 || K > (1 << 20) || K % 128 != 0) return MOE_EINVAL;
+    // One workgroup per (128-row tile, 256 columns); the grid must fit 2^31 - 1.
+    if (moe::gemm_max_tiles(max_rows, E) * (N / 256) >= kInt32Max) return MOE_EINVAL;
+    if (max_rows == 0) return MOE_OK;
+    if (!a || !a_scales || !expert_offsets || !w || !w_scales || !y || !workspace)
+        return MOE_ENULL;
+    if (!aligned(a, 16) || !aligned(w, 16) || !aligned(a_scales, 4) || !aligned(w_scales, 4) ||
+        !aligned(expert_offsets, 4) || !aligned(y, 8) || !aligned(workspace, 16))
+        return MOE_EALIGN;
+    if (workspace_bytes < moe::gemm_workspace_bytes(max_rows, E)) return MOE_ENOSPC;
+    moe::LaunchInfo info[2];
+    const hipError_t e = moe::launch_grouped_gemm_fp8(a, a_scales, expert_offsets, w, w_scales, E,
+                                                      N, K, max_rows, y, workspace,
+                                                      static_cast<hipStream_t>(stream), info);
+    if (log_enabled()) {
+        log_launch("gemm_tiles", info[0]);
+        log_launch("grouped_gemm_fp8", info[1]);
+    }
+    return status_of(e);
+}
+
 const char* moe_status_string(int status) {
     switch (status) {
         case MOE_OK: return "ok";

@@ -69,4 +69,13 @@ hipError_t launch_expert_scale(const void* disp, const float* disp_scales,
                                int E, bool fp8, bool identity, void* expert_out,
                                hipStream_t stream);
 
+// Grouped GEMM: tile-list workspace size and launcher (tile list + GEMM).
+size_t gemm_workspace_bytes(int64_t max_rows, int E);
+int64_t gemm_max_tiles(int64_t max_rows, int E);
+hipError_t launch_grouped_gemm_fp8(const void* a, const float* a_scales,
+                                   const int32_t* expert_offsets, const void* w,
+                                   const float* w_scales, int E, int N, int K, int64_t max_rows,
+                                   void* y, void* workspace, hipStream_t stream,
+                                   LaunchInfo info[2]);
+
 }  // namespace moe

@@ -215,6 +215,50 @@ int moe_combine_recv(const void* partial, const int32_t* partial_count,
                      int64_t T, int H, int k, void* y, void* stream);
 
 /*
+ * Grouped GEMM consumer of the FP8 segments (DeepSeek-V3 report excerpts on
+ * the fourth page: fine-grained quantisation with 1x128 activation tiles and
+ * 128x128 weight blocks, and the promotion of each 128-element interval's
+ * partial sum into higher-precision accumulators). For every expert e and
+ * every row r in [expert_offsets[e], expert_offsets[e+1]):
+ *
+ *   y[r, n] = bf16_RNE( sum_b a_scales[r, b] * w_scales[e, n/128, b]
+ *                       * sum_{k = 128b}^{128b+127} e4m3(a[r, k]) * e4m3(w[e, n, k]) )
+ *
+ * The partial of each interval comes from the matrix cores in fp32 (their
+ * internal summation of an interval is not exact IEEE fp32); it is scaled by
+ * the fp32 product of the two scales and added into an fp32 accumulator.
+ * Pad rows of a moe_dispatch segment have zero codes and zero scales, so
+ * their outputs are +0.
+ *
+ *   a               device E4M3 [max_rows, K]: moe_dispatch's out in FP8
+ *                   mode; 16-byte aligned
+ *   a_scales        device fp32 [max_rows, K/128]: moe_dispatch's out_scales
+ *   expert_offsets  device int32 [E+1]: moe_dispatch's expert_offsets (any
+ *                   row_align works; with 128 every 128-row tile is full).
+ *                   Segment ends are clamped to max_rows.
+ *   w               device E4M3 [E, N, K], K contiguous; 16-byte aligned
+ *   w_scales        device fp32 [E, N/128, K/128]
+ *   E, N, K         1 <= E <= 1024; 256 <= N <= 2^20 with N % 256 == 0;
+ *                   128 <= K <= 2^20 with K % 128 == 0
+ *   max_rows        rows of a, a_scales and y (the dispatch capacity,
+ *                   moe_dispatch_max_rows); 0 <= max_rows < 2^31
+ *   y               device bf16 [max_rows, N] out; 8-byte aligned. Rows at or
+ *                   past expert_offsets[E] are not written.
+ *   workspace       device, 16-byte aligned, at least
+ *                   moe_grouped_gemm_workspace_bytes(max_rows, E) bytes
+ *                   (the list of 128-row tiles, built on the device)
+ * The caller owns every buffer; nothing is kept between calls. Errors:
+ * MOE_EINVAL (limits), MOE_ENULL, MOE_EALIGN, MOE_ENOSPC (workspace),
+ * MOE_EHIP (launch). max_rows == 0 returns MOE_OK without a launch.
+ */
+size_t moe_grouped_gemm_workspace_bytes(int64_t max_rows, int E);
+
+int moe_grouped_gemm_fp8(const void* a, const float* a_scales, const int32_t* expert_offsets,
+                         const void* w, const float* w_scales, int E, int N, int K,
+                         int64_t max_rows, void* y, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
  * Stand-in experts for tests and the benchmark (not part of the path):
  * expert_out[r] = bf16(v * c_e) with c_e = fp32(e+1) / fp32(E) (or 1 when
  * identity != 0), e the expert of row r, v the bf16 row or, for FP8 rows,

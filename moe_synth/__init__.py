@@ -14,7 +14,16 @@ Kimi-K2 / Mixtral expert counts. No public dataset is involved; every array
 is drawn from numpy's PCG64 generator with the stream layout below.
 
 Streams: ``np.random.default_rng([seed, s])`` with s = 0 for activations,
-s = 1 for router logits, s = 2 for the Zipf popularity permutation.
+s = 1 for router logits, s = 2 for the Zipf popularity permutation, s = 3
+for fp32 expert weights, s = 4 for E4M3 weight codes, s = 5 for weight
+block scales.
+
+Expert weights for the grouped GEMM that consumes the FP8 segments come in
+two forms: fp32 normal weights with standard deviation 1/sqrt(K) (the tests
+quantise them), and already-quantised weights drawn directly as E4M3 codes,
+uniform over the 254 finite codes, with block scales uniform in
+[0.5, 1.5) * 2^-8 (for full-size runs, where quantising 7.5 GB on the host
+would take minutes; the GEMM's speed does not depend on the values).
 """
 from __future__ import annotations
 
@@ -32,6 +41,9 @@ __all__ = [
     "zipf_bias",
     "f32_to_bf16_bits",
     "bf16_bits_to_f32",
+    "gen_weights_f32",
+    "gen_fp8_weight_codes",
+    "gen_weight_scales",
 ]
 
 
@@ -121,3 +133,25 @@ def gen_logits(T: int, E: int, seed: int = 0, zipf_s: Optional[float] = None) ->
 def gen_inputs(w: Workload):
     """(x_bf16 uint16 [T,H], logits float32 [T,E]) for a workload."""
     return gen_x_bf16(w.T, w.H, w.seed), gen_logits(w.T, w.E, w.seed, w.zipf_s)
+
+
+def gen_weights_f32(E: int, N: int, K: int, seed: int = 0) -> np.ndarray:
+    """fp32 expert weights [E, N, K], N(0, 1/K) (a fan-in-scaled linear layer)."""
+    w = _rng(seed, 3).standard_normal((E, N, K), dtype=np.float32)
+    w *= np.float32(1.0 / np.sqrt(K))
+    return w
+
+
+def gen_fp8_weight_codes(E: int, N: int, K: int, seed: int = 0) -> np.ndarray:
+    """E4M3 codes [E, N, K], uniform over the 254 finite codes (0x7F and 0xFF,
+    the two NaN codes, never occur)."""
+    c = _rng(seed, 4).integers(0, 254, size=(E, N, K), dtype=np.uint8)
+    for ce in c:                      # per expert: no full-size temporaries
+        ce += (ce >= 0x7F).astype(np.uint8)
+    return c
+
+
+def gen_weight_scales(E: int, N: int, K: int, seed: int = 0) -> np.ndarray:
+    """fp32 block scales [E, N/128, K/128], uniform in [0.5, 1.5) * 2^-8."""
+    s = _rng(seed, 5).random((E, N // 128, K // 128), dtype=np.float32) + np.float32(0.5)
+    return s * np.float32(2.0 ** -8)

@@ -160,6 +160,49 @@ def test_combine_validation():
     assert c(T=0, eo=None, dr=None, w=None, y=None) == OK
 
 
+def test_grouped_gemm_workspace_bytes():
+    # 256 bytes of header (tile count), then one int4 per possible 128-row
+    # tile: ceil(max_rows / 128) + E (each segment adds at most one partial tile)
+    assert lib.moe_grouped_gemm_workspace_bytes(147584, 256) == 256 + (1153 + 256) * 16
+    assert lib.moe_grouped_gemm_workspace_bytes(1, 1) == 256 + 2 * 16
+    assert lib.moe_grouped_gemm_workspace_bytes(0, 8) == 256 + 8 * 16
+    assert lib.moe_grouped_gemm_workspace_bytes(-1, 8) == 0
+    assert lib.moe_grouped_gemm_workspace_bytes(100, 0) == 0
+    assert lib.moe_grouped_gemm_workspace_bytes(100, 1025) == 0
+
+
+def test_grouped_gemm_validation():
+    ws = lib.moe_grouped_gemm_workspace_bytes(1000, 8)
+
+    def g(**kw):
+        return lib.moe_grouped_gemm_fp8(
+            kw.get("a", A), kw.get("asc", B), kw.get("off", B + 4096), kw.get("w", A + 2 ** 24),
+            kw.get("wsc", B + 8192), kw.get("E", 8), kw.get("N", 512), kw.get("K", 256),
+            kw.get("R", 1000), kw.get("y", A + 2 ** 26), kw.get("ws", B + 2 ** 20),
+            kw.get("wsb", ws), None)
+    assert g(N=384) == EINVAL                  # N % 256
+    assert g(N=0) == EINVAL
+    assert g(N=2 ** 21) == EINVAL
+    assert g(K=200) == EINVAL                  # K % 128
+    assert g(K=0) == EINVAL
+    assert g(K=2 ** 21) == EINVAL
+    assert g(E=0) == EINVAL
+    assert g(E=1025) == EINVAL
+    assert g(R=-1) == EINVAL
+    assert g(R=2 ** 31) == EINVAL
+    assert g(R=2 ** 31 - 1, N=2 ** 20) == EINVAL    # launch grid too large
+    assert g(a=None) == ENULL
+    assert g(wsc=None) == ENULL
+    assert g(ws=None) == ENULL
+    assert g(a=A + 8) == EALIGN
+    assert g(w=A + 2 ** 24 + 4) == EALIGN
+    assert g(y=A + 2 ** 26 + 4) == EALIGN
+    assert g(asc=B + 2) == EALIGN
+    assert g(ws=B + 2 ** 20 + 8) == EALIGN
+    assert g(wsb=ws - 1) == ENOSPC
+    assert g(R=0, a=None, asc=None, off=None, w=None, wsc=None, y=None, ws=None) == OK
+
+
 def test_harness_validation():
     h = lambda **kw: lib.moe_harness_expert_scale(
         kw.get("disp", A), kw.get("sc", B), kw.get("rs", B + 4096), kw.get("idx", B + 8192),
