@@ -33,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
+PEAK_FP8_TFLOPS = 5000.0     # dense MFMA, fp8
 PROFILES = os.path.join(ROOT, "profiles")
 COMBINE_SRC = os.path.join(ROOT, "combine_moe_route_amd", "csrc", "combine.hip")
 SCATTER_SRC = os.path.join(ROOT, "combine_moe_route_amd", "csrc", "dispatch.hip")
@@ -210,6 +211,63 @@ def time_steps(step, steps, warmup, cold, scratch, stream):
         b.record(stream)
     torch.cuda.synchronize()
     return statistics.median([a.elapsed_time(b) * 1e3 for a, b in ev])
+
+
+def run_grouped_gemm(w, N, steps, warmup, cold=True):
+    """The grouped FP8 GEMM that consumes the dispatch's padded segments:
+    every expert's rows times that expert's [N, H] E4M3 weights (128x128
+    block scales). Weights are drawn on the device from a seeded torch
+    generator, uniform over the finite E4M3 codes (the GEMM's speed does not
+    depend on the values). Flops are counted on live rows only (2*T*k*N*H);
+    the pad rows the 128-row tiles also compute count against the rate."""
+    import torch
+
+    from combine_moe_route_amd import (alloc_dispatch, moe_dispatch, moe_grouped_gemm_fp8,
+                                       moe_grouped_gemm_workspace_bytes, moe_route_topk)
+    from moe_synth import gen_inputs
+
+    dev = torch.device("cuda:0")
+    x_np, l_np = gen_inputs(w)
+    x = torch.from_numpy(x_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    logits = torch.from_numpy(l_np).to(dev)
+    topk_idx, _ = moe_route_topk(logits, w.k)
+    bufs = alloc_dispatch(w.T, w.H, w.E, w.k, w.groups, w.row_align, True, dev)
+    moe_dispatch(x, topk_idx, w.E, w.groups, w.row_align, True, bufs)
+    a = bufs.out.view(torch.uint8)
+    g = torch.Generator(device=dev).manual_seed(w.seed)
+    wq = torch.randint(0, 254, (w.E, N, w.H), dtype=torch.uint8, device=dev, generator=g)
+    for e in range(w.E):                         # skip the NaN codes 0x7F, 0xFF
+        wq[e] += (wq[e] >= 0x7F).to(torch.uint8)
+    ws = (torch.rand((w.E, N // 128, w.H // 128), device=dev, generator=g) + 0.5) * 2.0 ** -8
+    R_cap = a.shape[0]
+    y = torch.empty((R_cap, N), dtype=torch.bfloat16, device=dev)
+    work = torch.empty(moe_grouped_gemm_workspace_bytes(R_cap, w.E), dtype=torch.uint8, device=dev)
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+    R = int(bufs.expert_offsets[-1].item())
+
+    def step():
+        moe_grouped_gemm_fp8(a, bufs.out_scales, bufs.expert_offsets, wq, ws, y, work)
+
+    us = time_steps(step, steps, warmup, cold, scratch, stream)
+    flops = 2.0 * w.T * w.k * N * w.H
+    flops_padded = 2.0 * R * N * w.H
+    tflops = flops / (us * 1e-6) / 1e12
+    hbm = w.E * N * w.H + w.E * (N // 128) * (w.H // 128) * 4 + R * w.H + R * (w.H // 128) * 4 \
+        + R * N * 2
+    return dict(
+        workload=w.name, N=N, K=w.H, rows=R, rows_live=w.T * w.k,
+        us=round(us, 1), tflops=round(tflops, 1),
+        tflops_padded_rows=round(flops_padded / (us * 1e-6) / 1e12, 1),
+        roofline={"kernel": "k_grouped_gemm_fp8", "bound": "mfma", "achieved": round(tflops, 1),
+                  "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                  "frac": round(tflops / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                  "flops_per_launch": flops},
+        hbm_bytes_algorithmic=hbm,
+        hbm_gbps_algorithmic=round(hbm / (us * 1e-6) / 1e9, 1),
+        weights="uniform finite E4M3 codes, block scales U[0.5,1.5)*2^-8 (seeded torch generator)",
+    )
 
 
 def run_routing_variants(steps, warmup, cold=True):
@@ -479,6 +537,10 @@ def main():
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the routing-variant measurements reported under 'next'")
     ap.add_argument("--cpu-tokens", type=int, default=16384)
+    ap.add_argument("--gemm-n", type=int, default=4096,
+                    help="output width of the grouped FP8 GEMM leg (0 skips it)")
+    ap.add_argument("--gemm-only", action="store_true",
+                    help="only run the grouped FP8 GEMM leg")
     ap.add_argument("--cu-budget", action="store_true",
                     help="only run the CU-budget / overlap experiment")
     ap.add_argument("--calib-copy", action="store_true",
@@ -505,6 +567,11 @@ def main():
         return
 
     w = WORKLOADS[args.workload]
+    if args.gemm_only:
+        print(json.dumps({"grouped_gemm_fp8": run_grouped_gemm(w, args.gemm_n or 4096, args.steps,
+                                                               args.warmup, cold=not args.warm)}),
+              flush=True)
+        return
     print(f"[bench] {w.name}: T={w.T} H={w.H} E={w.E} k={w.k} G={w.groups} A={w.row_align} "
           f"fp8={w.fp8} steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
     r = run_gpu(w, args.steps, args.warmup, cold=not args.warm, sender=True)
@@ -555,6 +622,10 @@ def main():
     if not args.no_variants:
         print("[bench] routing variants", file=sys.stderr, flush=True)
         out["next"].update(run_routing_variants(args.steps, args.warmup, cold=not args.warm))
+    if args.gemm_n and w.fp8:
+        print("[bench] grouped FP8 GEMM", file=sys.stderr, flush=True)
+        out["next"]["grouped_gemm_fp8"] = run_grouped_gemm(w, args.gemm_n, args.steps,
+                                                          args.warmup, cold=not args.warm)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens)

@@ -15,11 +15,18 @@
 //
 // Work split: segments are cut into 128-row tiles (a small kernel lists them
 // from the device-side offsets, so the host never reads them); a workgroup
-// computes a 128 x 256 output tile with 8 waves of 64 x 64. Both operands of
-// each 128-wide k-block are staged through LDS (XOR-swizzled 16-byte chunks,
-// double-buffered, one barrier per k-block).
+// computes a 128 x 256 output tile with 8 waves of 64 x 64. Each 128-wide
+// k-block of both operands and of the activation scales goes from memory
+// straight into LDS with buffer_load ... lds (no staging registers), into a
+// ring of three stages: k-block b+2 is in flight while b is computed. The
+// loads of b+2 are issued in pieces between the MFMA groups of b, so their
+// issue never holds the matrix pipe. One barrier per k-block; the wait before
+// it counts this wave's outstanding DMA explicitly, because the fence of
+// __syncthreads would drain the prefetch as well.
 #include "launch.h"
 #include "moe_device.h"
+
+#include <type_traits>
 
 namespace moe {
 namespace {
@@ -63,8 +70,13 @@ __global__ __launch_bounds__(kTileListThreads) void k_gemm_tiles(
     if (e == kTileListThreads - 1) count[0] = min(s_scan[e], max_tiles);
 }
 
+// LDS layout of a staged k-block: row-major 128-byte rows of 16-byte chunks,
+// chunk c of row r stored at chunk c ^ ((r >> 1) & 7). A fragment read has 16
+// lanes on 16 consecutive rows at the same logical chunk; even rows fall in
+// one half of the 64 banks and odd rows in the other, and the XOR spreads
+// each half's 8 rows over distinct 16-byte bank groups: no conflicts.
 __device__ __forceinline__ int swz(int row, int chunk) {
-    return row * kBK + ((chunk ^ (row & 7)) << 4);
+    return row * kBK + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
 __device__ __forceinline__ i32x8 frag(const uint8_t* s, int row, int half) {
@@ -73,6 +85,25 @@ __device__ __forceinline__ i32x8 frag(const uint8_t* s, int row, int half) {
     return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                  (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
+
+// Wait until at most n vector-memory operations of this wave are in flight
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt
+// left at their maxima, i.e. not waited for).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
+}
+
+// Workgroup barrier without the release/acquire fences of __syncthreads
+// (those would wait for every load in flight, including the LDS DMA of the
+// k-blocks being prefetched). The memory clobber keeps the compiler from
+// moving LDS accesses across it; completion of the DMA a wave needs is
+// waited for explicitly before it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+constexpr int kStages = 3;
+constexpr int kOpsPerStage = 7;    // per wave: 2 A + 4 W 16-byte DMA loads, 1 scale DMA load
 
 __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_fp8(
     const uint8_t* __restrict__ a, const float* __restrict__ a_scales,
@@ -89,61 +120,101 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_fp8(
     const int KB = K / kBK;
     const int n0 = nt * kBN;
 
-    __shared__ __attribute__((aligned(16))) uint8_t sA[2][kBM * kBK];
-    __shared__ __attribute__((aligned(16))) uint8_t sW[2][kBN * kBK];
+    // Three stages, each its own array so that the compiler can tell a DMA
+    // into one stage from reads of another.
+    __shared__ __attribute__((aligned(1024))) uint8_t sA0[kBM * kBK], sA1[kBM * kBK], sA2[kBM * kBK];
+    __shared__ __attribute__((aligned(1024))) uint8_t sW0[kBN * kBK], sW1[kBN * kBK], sW2[kBN * kBK];
+    // Activation scales of the k-block for each wave's 64 rows.
+    __shared__ __attribute__((aligned(256))) float sS0[8 * 64], sS1[8 * 64], sS2[8 * 64];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 2, wn = wave & 3;
 
-    // Rows past the tile's end read as zero through the descriptor bound.
     const __amdgpu_buffer_rsrc_t ra = range_rsrc(a + (int64_t)row0 * K, rows * K);
     const __amdgpu_buffer_rsrc_t rw = range_rsrc(w + ((int64_t)e * N + n0) * K, kBN * K);
     const __amdgpu_buffer_rsrc_t rsa = range_rsrc(a_scales + (int64_t)row0 * KB, rows * KB * 4);
     const float* wsc = w_scales + ((int64_t)e * (N / 128) + (n0 + wn * 64) / 128) * KB;
 
-    // Global -> register staging: A 2 x 16 B, W 4 x 16 B per thread.
-    int a_off[2], a_lds[2], w_off[4], w_lds[4];
+    // LDS DMA: each wave instruction fills 1 KB of a stage (64 lanes x 16 B,
+    // lane order). LDS 16-byte slot p of a stage is (row p/8, physical chunk
+    // p%8); the lane loads the logical chunk that the swizzle puts there.
+    int a_goff[2], w_goff[4];
 #pragma unroll
     for (int i = 0; i < 2; i++) {
-        const int idx = tid + i * kGemmThreads, r = idx >> 3, c = idx & 7;
-        a_off[i] = r * K + c * 16;
-        a_lds[i] = swz(r, c);
+        const int p = (wave * 2 + i) * 64 + lane, r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
+        a_goff[i] = r * K + c * 16;
     }
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        const int idx = tid + i * kGemmThreads, r = idx >> 3, c = idx & 7;
-        w_off[i] = r * K + c * 16;
-        w_lds[i] = swz(r, c);
+        const int p = (wave * 4 + i) * 64 + lane, r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
+        w_goff[i] = r * K + c * 16;
     }
-    // Activation-scale rows this lane needs: one per 16-row fragment.
-    int sa_off[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) sa_off[i] = (wm * 64 + i * 16 + (lane & 15)) * KB * 4;
+    // Scale DMA: lane l fetches the scale of the wave's row l (rows past the
+    // tile's end read 0 through the descriptor bound).
+    const int s_goff = (wm * 64 + lane) * KB * 4;
 
-    // Two register stages: k-block b+2 is fetched while b is computed and
-    // b+1 (fetched one k-block earlier) is written to the other LDS buffer.
-    u32x4 ga[2][2], gw[2][4];
-    float sa[2][4], sw[2];
-    auto fetch = [&](int st, int b) {
+    float sw[kStages];
+    auto stageA = [&](auto st) -> uint8_t* {
+        if constexpr (decltype(st)::value == 0) return sA0;
+        else if constexpr (decltype(st)::value == 1) return sA1;
+        else return sA2;
+    };
+    auto stageW = [&](auto st) -> uint8_t* {
+        if constexpr (decltype(st)::value == 0) return sW0;
+        else if constexpr (decltype(st)::value == 1) return sW1;
+        else return sW2;
+    };
+    auto stageS = [&](auto st) -> float* {
+        if constexpr (decltype(st)::value == 0) return sS0;
+        else if constexpr (decltype(st)::value == 1) return sS1;
+        else return sS2;
+    };
+    // Piece q (0..3) of a stage's DMA: q = 0: A row chunk 0 and W chunk 0,
+    // q = 1: A chunk 1 and W chunk 1, q = 2: W chunks 2 and 3, q = 3: scales.
+    auto issue_part = [&](auto st, int b, int q) {
+        constexpr int S = decltype(st)::value;
+        uint8_t* A = stageA(st);
+        uint8_t* W = stageW(st);
+        if (q < 2) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ra, (__attribute__((address_space(3))) void*)(A + (wave * 2 + q) * 1024), 16,
+                a_goff[q] + b * kBK, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rw, (__attribute__((address_space(3))) void*)(W + (wave * 4 + q) * 1024), 16,
+                w_goff[q] + b * kBK, 0, 0, 0);
+        } else if (q == 2) {
+#pragma unroll
+            for (int i = 2; i < 4; i++)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rw, (__attribute__((address_space(3))) void*)(W + (wave * 4 + i) * 1024), 16,
+                    w_goff[i] + b * kBK, 0, 0, 0);
+        } else {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsa, (__attribute__((address_space(3))) void*)(stageS(st) + wave * 64), 4,
+                s_goff + b * 4, 0, 0, 0);
+            sw[S] = wsc[b];
+        }
+    };
+    auto issue = [&](auto st, int b) {
+        constexpr int S = decltype(st)::value;
+        uint8_t* A = stageA(st);
+        uint8_t* W = stageW(st);
 #pragma unroll
         for (int i = 0; i < 2; i++)
-            ga[st][i] = __builtin_amdgcn_raw_buffer_load_b128(ra, a_off[i] + b * kBK, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ra, (__attribute__((address_space(3))) void*)(A + (wave * 2 + i) * 1024), 16,
+                a_goff[i] + b * kBK, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 4; i++)
-            gw[st][i] = __builtin_amdgcn_raw_buffer_load_b128(rw, w_off[i] + b * kBK, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-            sa[st][i] = __uint_as_float(
-                __builtin_amdgcn_raw_buffer_load_b32(rsa, sa_off[i] + b * 4, 0, 0));
-        sw[st] = wsc[b];
-    };
-    auto stash = [&](int st, int buf) {
-#pragma unroll
-        for (int i = 0; i < 2; i++) *reinterpret_cast<u32x4*>(&sA[buf][a_lds[i]]) = ga[st][i];
-#pragma unroll
-        for (int i = 0; i < 4; i++) *reinterpret_cast<u32x4*>(&sW[buf][w_lds[i]]) = gw[st][i];
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rw, (__attribute__((address_space(3))) void*)(W + (wave * 4 + i) * 1024), 16,
+                w_goff[i] + b * kBK, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsa, (__attribute__((address_space(3))) void*)(stageS(st) + wave * 64), 4,
+            s_goff + b * 4, 0, 0, 0);
+        sw[S] = wsc[b];
     };
 
     f32x4 acc[4][4];
@@ -153,48 +224,72 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_fp8(
         for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int half = lane >> 4;
-    auto compute = [&](int buf, const float* fs) {
-        i32x8 xf[4], wf[4];
-#pragma unroll
-        for (int i = 0; i < 4; i++) xf[i] = frag(sA[buf], wm * 64 + i * 16 + (lane & 15), half);
-#pragma unroll
-        for (int j = 0; j < 4; j++) wf[j] = frag(sW[buf], wn * 64 + j * 16 + (lane & 15), half);
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const f32x4 p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    wf[j], xf[i], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-                for (int r = 0; r < 4; r++) acc[i][j][r] = fmaf(p[r], fs[i], acc[i][j][r]);
-            }
-    };
-
-    fetch(0, 0);
-    if (KB > 1) fetch(1, 1);
-    stash(0, 0);
-    __syncthreads();
-
-    // Stage st of the registers holds k-block b while b is computed from LDS
-    // buffer b & 1; the loop body is written out for b even and b odd so
-    // that every register index is a constant.
-    for (int b = 0; b < KB; b += 2) {
+    auto compute = [&](auto st, auto nst, int nb) {
+        constexpr int S = decltype(st)::value;
+        const uint8_t* A = stageA(st);
+        const uint8_t* W = stageW(st);
+        const float* Ssc = stageS(st) + wave * 64;
         float f[4];
 #pragma unroll
-        for (int i = 0; i < 4; i++) f[i] = sa[0][i] * sw[0];
-        if (b + 2 < KB) fetch(0, b + 2);
-        compute(0, f);
-        if (b + 1 < KB) stash(1, 1);
-        __syncthreads();
-        if (b + 1 >= KB) break;
-
+        for (int i = 0; i < 4; i++) f[i] = Ssc[i * 16 + (lane & 15)] * sw[S];
+        i32x8 xf[4], wf[4];
 #pragma unroll
-        for (int i = 0; i < 4; i++) f[i] = sa[1][i] * sw[1];
-        if (b + 3 < KB) fetch(1, b + 3);
-        compute(1, f);
-        if (b + 2 < KB) stash(0, 0);
-        __syncthreads();
+        for (int j = 0; j < 4; j++) wf[j] = frag(W, wn * 64 + j * 16 + (lane & 15), half);
+#pragma unroll
+        for (int i = 0; i < 4; i++) xf[i] = frag(A, wm * 64 + i * 16 + (lane & 15), half);
+        // Row group i: four MFMAs; their results are promoted while the next
+        // group's MFMAs run (two groups of partials live at a time).
+        f32x4 prev[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            f32x4 cur[4];
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                cur[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    wf[j], xf[i], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+            issue_part(nst, nb, i);
+            if (i > 0) {
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+#pragma unroll
+                    for (int r = 0; r < 4; r++)
+                        acc[i - 1][j][r] = fmaf(prev[j][r], f[i - 1], acc[i - 1][j][r]);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; j++) prev[j] = cur[j];
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) acc[3][j][r] = fmaf(prev[j][r], f[3], acc[3][j][r]);
+    };
+
+    // One k-block: its stage's DMA (this wave's part) is complete once at most
+    // the next k-block's operations are in flight; the barrier then makes
+    // every wave's part visible and guarantees that all waves are done with
+    // the stage the new prefetch overwrites (read in the previous step). The
+    // prefetch is always issued, clamped to the last k-block, so the loop has
+    // one shape; the clamped copies land in a stage that is never read.
+    auto step = [&](auto st, int b) {
+        constexpr int S = decltype(st)::value;
+        wait_vmcnt<kOpsPerStage>();
+        lds_barrier();
+        compute(st, std::integral_constant<int, (S + 2) % kStages>{}, min(b + 2, KB - 1));
+    };
+
+    issue(std::integral_constant<int, 0>{}, 0);
+    issue(std::integral_constant<int, 1>{}, min(1, KB - 1));
+    int b = 0;
+    for (; b + kStages <= KB; b += kStages) {
+        step(std::integral_constant<int, 0>{}, b);
+        step(std::integral_constant<int, 1>{}, b + 1);
+        step(std::integral_constant<int, 2>{}, b + 2);
     }
+    if (b < KB) step(std::integral_constant<int, 0>{}, b);
+    if (b + 1 < KB) step(std::integral_constant<int, 1>{}, b + 1);
+    // No LDS DMA may still be writing when the workgroup's LDS is released.
+    wait_vmcnt<0>();
 
     // Lane holds, for fragment pair (i, j), row 16i + lane%16 and the four
     // consecutive columns 16j + 4*(lane/16) .. +3.
