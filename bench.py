@@ -37,6 +37,7 @@ PEAK_FP8_TFLOPS = 5000.0     # dense MFMA, fp8
 PROFILES = os.path.join(ROOT, "profiles")
 COMBINE_SRC = os.path.join(ROOT, "combine_moe_route_amd", "csrc", "combine.hip")
 SCATTER_SRC = os.path.join(ROOT, "combine_moe_route_amd", "csrc", "dispatch.hip")
+GEMM_SRC = os.path.join(ROOT, "combine_moe_route_amd", "csrc", "grouped_gemm.hip")
 
 
 def algorithmic_bytes(T, H, E, k, R, fp8):
@@ -262,7 +263,8 @@ def run_grouped_gemm(w, N, steps, warmup, cold=True):
         tflops_padded_rows=round(flops_padded / (us * 1e-6) / 1e12, 1),
         roofline={"kernel": "k_grouped_gemm_fp8", "bound": "mfma", "achieved": round(tflops, 1),
                   "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                  "frac": round(tflops / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                  "frac": round(tflops / PEAK_FP8_TFLOPS, 4),
+                  "traffic": read_traffic("k_grouped_gemm_fp8", "grouped_gemm_" + w.name, GEMM_SRC),
                   "flops_per_launch": flops},
         hbm_bytes_algorithmic=hbm,
         hbm_gbps_algorithmic=round(hbm / (us * 1e-6) / 1e9, 1),
