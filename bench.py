@@ -272,6 +272,71 @@ def run_grouped_gemm(w, N, steps, warmup, cold=True):
     )
 
 
+def run_graph(w, steps):
+    """Route + dispatch + combine captured once in a HIP graph and replayed:
+    the GPU-side time of a launch-bound step without the host's per-launch
+    cost. warm = events around `steps` back-to-back replays; cold = one event
+    pair per replay with the 1 GiB write before it."""
+    import torch
+
+    from combine_moe_route_amd import (alloc_dispatch, moe_combine, moe_dispatch,
+                                       moe_dispatch_max_rows, moe_harness_expert_scale,
+                                       moe_route_topk)
+    from moe_synth import gen_inputs
+
+    dev = torch.device("cuda:0")
+    x_np, l_np = gen_inputs(w)
+    x = torch.from_numpy(x_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    logits = torch.from_numpy(l_np).to(dev)
+    topk_idx = torch.empty((w.T, w.k), dtype=torch.int32, device=dev)
+    topk_w = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
+    bufs = alloc_dispatch(w.T, w.H, w.E, w.k, w.groups, w.row_align, w.fp8, dev)
+    cap = moe_dispatch_max_rows(w.T, w.E, w.k, w.row_align)
+    expert_out = torch.empty((cap, w.H), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev)
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    moe_route_topk(logits, w.k, topk_idx, topk_w)
+    moe_dispatch(x, topk_idx, w.E, w.groups, w.row_align, w.fp8, bufs)
+    moe_harness_expert_scale(bufs, topk_idx, w.E, w.fp8, expert_out=expert_out)
+
+    def step():
+        moe_route_topk(logits, w.k, topk_idx, topk_w)
+        moe_dispatch(x, topk_idx, w.E, w.groups, w.row_align, w.fp8, bufs)
+        moe_combine(expert_out, bufs.dst_row, topk_w, y)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(20):
+        g.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    warm = e0.elapsed_time(e1) * 1e3 / steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(min(steps, 200))]
+    for a, b in ev:
+        scratch.fill_(1)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+    torch.cuda.synchronize()
+    cold = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    return dict(us_total_warm_mean=round(warm, 2), us_total_cold=round(statistics.median(cold), 2),
+                us_total_cold_p10=round(pct(cold, 10), 2), us_total_cold_p90=round(pct(cold, 90), 2))
+
+
 def run_routing_variants(steps, warmup, cold=True):
     """Shared expert on the 16384-token FP8 workload; load-proportional
     replicas on the skewed 4096-token workload."""
@@ -534,6 +599,9 @@ def main():
     ap.add_argument("--workload", default="dsv3_prefill")
     ap.add_argument("--also", default="kimi_prefill",
                     help="comma-separated extra workloads reported under 'other' ('' for none)")
+    ap.add_argument("--decode", default="mixtral_decode,dsv3_decode",
+                    help="decode workloads reported under 'decode', cold and warm ('' for none)")
+    ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--warm", action="store_true", help="skip the cache flush between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
@@ -585,6 +653,20 @@ def main():
         wo = WORKLOADS[name]
         print(f"[bench] {name}", file=sys.stderr, flush=True)
         others[name] = summarize(wo, run_gpu(wo, args.steps, args.warmup, cold=not args.warm))
+    # Decode batches (128 tokens): launch- and latency-bound, their working
+    # sets fit the 256 MB Infinity Cache, so both a cold (1 GiB write before
+    # each step) and a warm figure are given.
+    decode = {}
+    for name in [n for n in args.decode.split(",") if n]:
+        wd = WORKLOADS[name]
+        print(f"[bench] {name} (decode, {args.decode_steps} steps)", file=sys.stderr, flush=True)
+        cold_s = summarize(wd, run_gpu(wd, args.decode_steps, 20, cold=True))
+        warm_s = summarize(wd, run_gpu(wd, args.decode_steps, 20, cold=False))
+        keys = ("us_route", "us_dispatch", "us_combine", "us_total", "us_total_p10",
+                "us_total_p90", "gbps")
+        decode[name] = dict(rows=cold_s["rows"], bytes_total=cold_s["bytes_dispatch"] + cold_s["bytes_combine"],
+                            cold={k: cold_s[k] for k in keys}, warm={k: warm_s[k] for k in keys},
+                            graph=run_graph(wd, args.decode_steps))
     copy_gbps = round(copy_bandwidth(), 1)
 
     comb_avg_us = statistics.mean(r["comb"])
@@ -619,6 +701,7 @@ def main():
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic, "us_avg": round(comb_avg_us, 2)},
         "other": others,
+        "decode": decode,
         "next": {"sender_side_combine": r.get("sender")},
     }
     if not args.no_variants:
