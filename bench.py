@@ -418,9 +418,14 @@ def run_routing_variants(steps, warmup, cold=True):
     return res
 
 
-def cu_budget(w, steps):
+def cu_budget(w, steps, co="bf16"):
     """Dispatch + combine restricted to N CUs through CU-masked streams, and
-    the same steps overlapped with a bf16 GEMM confined to the other CUs."""
+    the same steps overlapped with a GEMM confined to the other CUs. co =
+    "bf16": a plain 8192^3 bf16 GEMM (torch.matmul); co = "grouped": the
+    grouped FP8 GEMM of the expert projection (N = 4096) on a second
+    micro-batch's dispatch output (seed + 1), i.e. one micro-batch's experts
+    running while the other's dispatch and combine run. The last row (CUs 0)
+    runs both on plain streams that share every CU."""
     import ctypes
 
     import torch
@@ -458,9 +463,29 @@ def cu_budget(w, steps):
     moe_dispatch(x, idx, w.E, w.groups, w.row_align, w.fp8, bufs)
     moe_harness_expert_scale(bufs, idx, w.E, w.fp8, expert_out=eo)
     gen = torch.Generator(device=dev).manual_seed(0)
-    ga = torch.randn((8192, 8192), dtype=torch.bfloat16, device=dev, generator=gen)
-    gb = torch.randn((8192, 8192), dtype=torch.bfloat16, device=dev, generator=gen)
-    gc = torch.empty((8192, 8192), dtype=torch.bfloat16, device=dev)
+    if co == "grouped":
+        from combine_moe_route_amd import moe_grouped_gemm_fp8, moe_grouped_gemm_workspace_bytes
+        w2 = w.with_(seed=w.seed + 1)
+        x2_np, l2_np = gen_inputs(w2)
+        x2 = torch.from_numpy(x2_np.view(np.int16)).view(torch.bfloat16).to(dev)
+        idx2, _ = moe_route_topk(torch.from_numpy(l2_np).to(dev), w.k)
+        bufs2 = alloc_dispatch(w.T, w.H, w.E, w.k, w.groups, w.row_align, True, dev)
+        moe_dispatch(x2, idx2, w.E, w.groups, w.row_align, True, bufs2)
+        a2 = bufs2.out.view(torch.uint8)
+        gemm_n = 4096
+        wq = torch.randint(0, 254, (w.E, gemm_n, w.H), dtype=torch.uint8, device=dev, generator=gen)
+        for e in range(w.E):
+            wq[e] += (wq[e] >= 0x7F).to(torch.uint8)
+        wsc = (torch.rand((w.E, gemm_n // 128, w.H // 128), device=dev, generator=gen) + 0.5) * 2.0 ** -8
+        y2 = torch.empty((a2.shape[0], gemm_n), dtype=torch.bfloat16, device=dev)
+        work2 = torch.empty(moe_grouped_gemm_workspace_bytes(a2.shape[0], w.E), dtype=torch.uint8,
+                            device=dev)
+        gemm_name = f"grouped FP8 GEMM, second micro-batch (seed {w2.seed}), N {gemm_n}, K {w.H}"
+    else:
+        ga = torch.randn((8192, 8192), dtype=torch.bfloat16, device=dev, generator=gen)
+        gb = torch.randn((8192, 8192), dtype=torch.bfloat16, device=dev, generator=gen)
+        gc = torch.empty((8192, 8192), dtype=torch.bfloat16, device=dev)
+        gemm_name = "bf16 8192x8192x8192 (torch.matmul)"
     torch.cuda.synchronize()
 
     def moe_step():
@@ -469,7 +494,10 @@ def cu_budget(w, steps):
         moe_combine(eo, bufs.dst_row, wt, y)
 
     def gemm():
-        torch.matmul(ga, gb, out=gc)
+        if co == "grouped":
+            moe_grouped_gemm_fp8(a2, bufs2.out_scales, bufs2.expert_offsets, wq, wsc, y2, work2)
+        else:
+            torch.matmul(ga, gb, out=gc)
 
     def timed(fn, reps, stream):
         with torch.cuda.stream(stream):
@@ -487,18 +515,25 @@ def cu_budget(w, steps):
     t_gemm_full = timed(gemm, steps, full)
     gemm_reps = max(1, round(steps * t_moe_full / t_gemm_full))
     rows = []
-    for n in (32, 64, 128, 192, 256):
+    for n in (32, 64, 128, 192, 256, 0):
         # consecutive mask bits are spread over the XCDs (a mask that leaves an
-        # XCD without CUs is rejected), so [0, n) is an even n-CU budget
-        cus = list(range(min(n, n_cu)))
-        rest = list(range(min(n, n_cu), n_cu))
+        # XCD without CUs is rejected), so [0, n) is an even n-CU budget;
+        # n = 0: two plain streams, both free to use every CU
         print(f"[bench] cu budget {n}", file=sys.stderr, flush=True)
-        s_moe = masked(cus)
-        t_moe = timed(moe_step, steps, s_moe)
-        row = dict(cus=n, us_moe_step=round(t_moe, 1))
+        if n == 0:
+            s_moe, s_rest = torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)
+            rest = True
+            t_moe, t_gemm = t_moe_full, t_gemm_full
+        else:
+            cus = list(range(min(n, n_cu)))
+            rest = list(range(min(n, n_cu), n_cu))
+            s_moe = masked(cus)
+            t_moe = timed(moe_step, steps, s_moe)
+        row = dict(cus=n if n else "all (shared)", us_moe_step=round(t_moe, 1))
         if rest:
-            s_rest = masked(rest)
-            t_gemm = timed(gemm, gemm_reps, s_rest)
+            if n:
+                s_rest = masked(rest)
+                t_gemm = timed(gemm, gemm_reps, s_rest)
             # overlap: both streams start after one marker, run concurrently
             start = torch.cuda.Event()
             start.record(full)
@@ -526,7 +561,7 @@ def cu_budget(w, steps):
         torch.cuda.synchronize()
         while made:
             hip.hipStreamDestroy(made.pop())
-    return dict(workload=w.name, moe_steps=steps, gemm="bf16 8192x8192x8192", gemm_reps=gemm_reps,
+    return dict(workload=w.name, moe_steps=steps, gemm=gemm_name, gemm_reps=gemm_reps,
                 us_moe_step_full_gpu=round(t_moe_full, 1), us_gemm_full_gpu=round(t_gemm_full, 1),
                 budgets=rows)
 
@@ -613,6 +648,8 @@ def main():
                     help="only run the grouped FP8 GEMM leg")
     ap.add_argument("--cu-budget", action="store_true",
                     help="only run the CU-budget / overlap experiment")
+    ap.add_argument("--cu-budget-gemm", default="bf16", choices=("bf16", "grouped"),
+                    help="co-runner of the CU-budget experiment")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run 1 GiB device copies (counter calibration)")
     args = ap.parse_args()
@@ -628,7 +665,8 @@ def main():
     from moe_synth import WORKLOADS
 
     if args.cu_budget:
-        print(json.dumps({"cu_budget": cu_budget(WORKLOADS[args.workload], args.steps)}), flush=True)
+        print(json.dumps({"cu_budget": cu_budget(WORKLOADS[args.workload], args.steps,
+                                                 args.cu_budget_gemm)}), flush=True)
         return
 
     if args.calib_copy:
