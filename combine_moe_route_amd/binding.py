@@ -312,6 +312,10 @@ def moe_harness_expert_scale(bufs: DispatchBuffers, topk_idx: torch.Tensor, E: i
     if expert_out is None:
         expert_out = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
     _need(expert_out, "expert_out", torch.bfloat16, (R, H), dev)
+    if topk_idx.numel() == 0:
+        # no tokens: the dispatch used no rows, so there is nothing to fill
+        # (and torch hands out no address for the empty routing table)
+        return expert_out
     _check("moe_harness_expert_scale", lib.moe_harness_expert_scale(
         _ptr(bufs.out), _ptr(bufs.out_scales) if fp8 else None, _ptr(bufs.row_src),
         _ptr(topk_idx), _ptr(bufs.expert_offsets), R, H, E,
