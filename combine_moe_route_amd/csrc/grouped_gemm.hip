@@ -198,23 +198,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_fp8(
         }
     };
     auto issue = [&](auto st, int b) {
-        constexpr int S = decltype(st)::value;
-        uint8_t* A = stageA(st);
-        uint8_t* W = stageW(st);
 #pragma unroll
-        for (int i = 0; i < 2; i++)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                ra, (__attribute__((address_space(3))) void*)(A + (wave * 2 + i) * 1024), 16,
-                a_goff[i] + b * kBK, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rw, (__attribute__((address_space(3))) void*)(W + (wave * 4 + i) * 1024), 16,
-                w_goff[i] + b * kBK, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rsa, (__attribute__((address_space(3))) void*)(stageS(st) + wave * 64), 4,
-            s_goff + b * 4, 0, 0, 0);
-        sw[S] = wsc[b];
+        for (int q = 0; q < 4; q++) issue_part(st, b, q);
     };
 
     f32x4 acc[4][4];
