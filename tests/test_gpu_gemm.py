@@ -134,6 +134,21 @@ def test_gemm_exact_intervals_tight_tolerance(E, K, N, seed):
     assert same >= 0.999
 
 
+def test_gemm_deep_inner_dimension():
+    """K = 16384 (128 k-blocks: many rounds of the three-stage ring)."""
+    rng = np.random.default_rng(12)
+    E, K, N = 2, 16384, 256
+    off = np.array([0, 40, 64], np.int32)
+    R = 70
+    a = gen_fp8_weight_codes(1, R, K, 31)[0]
+    a_s = rng.uniform(0.5, 1.5, size=(R, K // 128)).astype(np.float32)
+    w = gen_fp8_weight_codes(E, N, K, 32)
+    w_s = gen_weight_scales(E, N, K, 32)
+    g = oracle.grouped_gemm_fp8(a, a_s, off, w, w_s)
+    y = run_gpu(a, a_s, off, w, w_s)
+    check(y, g, off, K)
+
+
 def test_gemm_empty_experts_and_single_expert():
     rng = np.random.default_rng(7)
     K, N = 256, 256

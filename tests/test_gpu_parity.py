@@ -269,6 +269,8 @@ def test_router_more_than_64_experts_per_token(dev, E, k):
     Case(T=300, H=512, E=128, k=65, groups=4, row_align=8, seed=21),                 # bf16, k > 64
     Case(T=257, H=1024, E=64, k=12, groups=8, row_align=128, fp8=True, seed=22),     # FP8, k > 8
     Case(T=100, H=256, E=512, k=100, groups=16, row_align=4, fp8=True, seed=23),     # FP8, k > 64
+    Case(T=50, H=16384, E=32, k=8, groups=4, row_align=128, fp8=True, seed=24),     # FP8, > 16 chunks per row
+    Case(T=33, H=16384, E=16, k=4, seed=25),                                          # bf16, 16 K wide rows
     Case(T=50, H=20480, E=16, k=4, groups=2, row_align=2, fp8=True, seed=24),        # FP8, > 16 waves per row
 ], ids=lambda c: c.label())
 def test_many_slots_and_wide_rows(dev, c):
