@@ -13,16 +13,18 @@
 // registers. On gfx950 one v_mfma_f32_16x16x128_f8f6f4 covers exactly one
 // interval for a 16x16 output tile, so each MFMA result is promoted at once.
 //
-// Work split: segments are cut into 128-row tiles (a small kernel lists them
+// Work split: segments are cut into row tiles (a small kernel lists them
 // from the device-side offsets, so the host never reads them); a workgroup
-// computes a 128 x 256 output tile with 8 waves of 64 x 64. Each 128-wide
-// k-block of both operands and of the activation scales goes from memory
-// straight into LDS with buffer_load ... lds (no staging registers), into a
-// ring of three stages: k-block b+2 is in flight while b is computed. The
-// loads of b+2 are issued in pieces between the MFMA groups of b, so their
-// issue never holds the matrix pipe. One barrier per k-block; the wait before
-// it counts this wave's outstanding DMA explicitly, because the fence of
-// __syncthreads would drain the prefetch as well.
+// computes one tile of 256 output columns with 8 waves. Tiles are 256 rows
+// when the capacity holds prefill-sized segments and 128 rows otherwise (the
+// shapes are described at Shape below). Each 128-wide k-block of both
+// operands and of the activation scales goes from memory straight into LDS
+// with buffer_load ... lds (no staging registers), into a ring of stages, and
+// the loads of a later k-block are issued in pieces between the MFMA groups
+// of the current one, so their issue never holds the matrix pipe. One barrier
+// per k-block; the wait before it counts this wave's outstanding DMA
+// explicitly, because the fence of __syncthreads would drain the prefetch as
+// well.
 #include "launch.h"
 #include "moe_device.h"
 
@@ -31,7 +33,7 @@
 namespace moe {
 namespace {
 
-constexpr int kBM = 128;             // rows per tile
+constexpr int kBMin = 128;           // rows per tile of the smaller shape (sizes the tile list)
 constexpr int kBN = 256;             // output columns per tile
 constexpr int kBK = 128;             // inner-dimension block (one scale interval)
 constexpr int kGemmThreads = 512;    // 8 waves: 2 along rows x 4 along columns
@@ -40,13 +42,13 @@ constexpr int kTileListThreads = 1024;
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Tile list: tile t covers rows [row0, min(row0 + kBM, seg_end)) of expert e.
+// Tile list: tile t covers rows [row0, min(row0 + bm, seg_end)) of expert e.
 // Packed as int4 {row0, seg_end, e, 0}. Segment bounds are clamped to the
 // row capacity, so no tile reaches past the buffers whatever the offsets
 // hold. count[0] = number of tiles (at most max_tiles, which the host derives
 // from the capacity).
 __global__ __launch_bounds__(kTileListThreads) void k_gemm_tiles(
-    const int32_t* __restrict__ off, int E, int max_rows, int max_tiles,
+    const int32_t* __restrict__ off, int E, int max_rows, int max_tiles, int bm,
     int4* __restrict__ tiles, int32_t* __restrict__ count) {
     __shared__ int s_scan[kTileListThreads];
     const int e = threadIdx.x;
@@ -54,7 +56,7 @@ __global__ __launch_bounds__(kTileListThreads) void k_gemm_tiles(
     if (e < E) {
         r0 = min(max(off[e], 0), max_rows);
         r1 = min(max(off[e + 1], 0), max_rows);
-        nt = r1 > r0 ? (r1 - r0 + kBM - 1) / kBM : 0;
+        nt = r1 > r0 ? (r1 - r0 + bm - 1) / bm : 0;
     }
     s_scan[e] = nt;
     __syncthreads();
@@ -66,7 +68,7 @@ __global__ __launch_bounds__(kTileListThreads) void k_gemm_tiles(
     }
     const int base = s_scan[e] - nt;
     for (int i = 0; i < nt && base + i < max_tiles; i++)
-        tiles[base + i] = make_int4(r0 + i * kBM, r1, e, 0);
+        tiles[base + i] = make_int4(r0 + i * bm, r1, e, 0);
     if (e == kTileListThreads - 1) count[0] = min(s_scan[e], max_tiles);
 }
 
@@ -102,27 +104,46 @@ __device__ __forceinline__ void wait_vmcnt() {
 // waited for explicitly before it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-constexpr int kStages = 3;
-constexpr int kOpsPerStage = 7;    // per wave: 2 A + 4 W 16-byte DMA loads, 1 scale DMA load
+// Tile shapes. Both use 8 waves and 256 output columns; the row count picks
+// the rest:
+//   128 rows: 2 x 4 waves of 64 x 64, three LDS stages (48 KB each), two
+//             k-blocks in flight while one is computed;
+//   256 rows: 4 x 2 waves of 64 x 128, two LDS stages (64 KB each). Each
+//             k-block is twice the work, which covers the load of the next
+//             one, and every loaded byte feeds twice the MFMAs. W fragments
+//             are read in two halves of 64 columns to stay within 256 VGPRs.
+template <int BM>
+struct Shape {
+    static constexpr int kWavesM = BM / 64;              // 2 or 4
+    static constexpr int kWavesN = 8 / kWavesM;          // 4 or 2
+    static constexpr int kWaveCols = kBN / kWavesN;      // 64 or 128
+    static constexpr int kHalves = kWaveCols / 64;       // W fragment halves: 1 or 2
+    static constexpr int kStages = BM == 128 ? 3 : 2;
+    static constexpr int kAChunks = BM / 64;             // 1 KB A chunks per wave and stage
+    static constexpr int kOps = kAChunks + 4 + 1;        // DMA loads per wave and stage
+};
 
-__global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_fp8(
+template <int BM>
+__device__ __forceinline__ void gemm_body(
     const uint8_t* __restrict__ a, const float* __restrict__ a_scales,
     const uint8_t* __restrict__ w, const float* __restrict__ w_scales,
     const int4* __restrict__ tiles, const int32_t* __restrict__ tile_count,
     uint16_t* __restrict__ y, int N, int K) {
+    using SH = Shape<BM>;
+    constexpr int kStages = SH::kStages;
     const int n_tiles_n = N / kBN;
     const int tile = blockIdx.x / n_tiles_n;
     const int nt = blockIdx.x - tile * n_tiles_n;
     if (tile >= tile_count[0]) return;
     const int4 td = tiles[tile];
     const int row0 = td.x, e = td.z;
-    const int rows = min(kBM, td.y - row0);
+    const int rows = min(BM, td.y - row0);
     const int KB = K / kBK;
     const int n0 = nt * kBN;
 
-    // Three stages, each its own array so that the compiler can tell a DMA
-    // into one stage from reads of another.
-    __shared__ __attribute__((aligned(1024))) uint8_t sA0[kBM * kBK], sA1[kBM * kBK], sA2[kBM * kBK];
+    // One array per stage, so that the compiler can tell a DMA into one stage
+    // from reads of another (the third stage is used by 128-row tiles only).
+    __shared__ __attribute__((aligned(1024))) uint8_t sA0[BM * kBK], sA1[BM * kBK], sA2[BM * kBK];
     __shared__ __attribute__((aligned(1024))) uint8_t sW0[kBN * kBK], sW1[kBN * kBK], sW2[kBN * kBK];
     // Activation scales of the k-block for each wave's 64 rows.
     __shared__ __attribute__((aligned(256))) float sS0[8 * 64], sS1[8 * 64], sS2[8 * 64];
@@ -130,26 +151,28 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_fp8(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 2, wn = wave & 3;
+    const int wm = wave / SH::kWavesN, wn = wave % SH::kWavesN;
 
+    // Rows past the tile's end read as zero through the descriptor bound.
     const __amdgpu_buffer_rsrc_t ra = range_rsrc(a + (int64_t)row0 * K, rows * K);
     const __amdgpu_buffer_rsrc_t rw = range_rsrc(w + ((int64_t)e * N + n0) * K, kBN * K);
     const __amdgpu_buffer_rsrc_t rsa = range_rsrc(a_scales + (int64_t)row0 * KB, rows * KB * 4);
-    const float* wsc = w_scales + ((int64_t)e * (N / 128) + (n0 + wn * 64) / 128) * KB;
+    const float* wsc =
+        w_scales + ((int64_t)e * (N / 128) + (n0 + wn * SH::kWaveCols) / 128) * KB;
 
     // LDS DMA: each wave instruction fills 1 KB of a stage (64 lanes x 16 B,
     // lane order). LDS 16-byte slot p of a stage is (row p/8, physical chunk
     // p%8); the lane loads the logical chunk that the swizzle puts there.
-    int a_goff[2], w_goff[4];
+    int a_goff[SH::kAChunks], w_goff[4];
 #pragma unroll
-    for (int i = 0; i < 2; i++) {
-        const int p = (wave * 2 + i) * 64 + lane, r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
-        a_goff[i] = r * K + c * 16;
+    for (int i = 0; i < SH::kAChunks; i++) {
+        const int p = (wave * SH::kAChunks + i) * 64 + lane, r = p >> 3;
+        a_goff[i] = r * K + (((p & 7) ^ ((r >> 1) & 7)) << 4);
     }
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        const int p = (wave * 4 + i) * 64 + lane, r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
-        w_goff[i] = r * K + c * 16;
+        const int p = (wave * 4 + i) * 64 + lane, r = p >> 3;
+        w_goff[i] = r * K + (((p & 7) ^ ((r >> 1) & 7)) << 4);
     }
     // Scale DMA: lane l fetches the scale of the wave's row l (rows past the
     // tile's end read 0 through the descriptor bound).
@@ -171,26 +194,20 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_fp8(
         else if constexpr (decltype(st)::value == 1) return sS1;
         else return sS2;
     };
-    // Piece q (0..3) of a stage's DMA: q = 0: A row chunk 0 and W chunk 0,
-    // q = 1: A chunk 1 and W chunk 1, q = 2: W chunks 2 and 3, q = 3: scales.
+    // Piece q (0..3) of a stage's DMA: W chunk q, a share of the A chunks
+    // (all of them over the four pieces) and, with q = 3, the scales.
     auto issue_part = [&](auto st, int b, int q) {
         constexpr int S = decltype(st)::value;
         uint8_t* A = stageA(st);
         uint8_t* W = stageW(st);
-        if (q < 2) {
+        for (int i = q * SH::kAChunks / 4; i < (q + 1) * SH::kAChunks / 4; i++)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                ra, (__attribute__((address_space(3))) void*)(A + (wave * 2 + q) * 1024), 16,
-                a_goff[q] + b * kBK, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rw, (__attribute__((address_space(3))) void*)(W + (wave * 4 + q) * 1024), 16,
-                w_goff[q] + b * kBK, 0, 0, 0);
-        } else if (q == 2) {
-#pragma unroll
-            for (int i = 2; i < 4; i++)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rw, (__attribute__((address_space(3))) void*)(W + (wave * 4 + i) * 1024), 16,
-                    w_goff[i] + b * kBK, 0, 0, 0);
-        } else {
+                ra, (__attribute__((address_space(3))) void*)(A + (wave * SH::kAChunks + i) * 1024),
+                16, a_goff[i] + b * kBK, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rw, (__attribute__((address_space(3))) void*)(W + (wave * 4 + q) * 1024), 16,
+            w_goff[q] + b * kBK, 0, 0, 0);
+        if (q == 3) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rsa, (__attribute__((address_space(3))) void*)(stageS(st) + wave * 64), 4,
                 s_goff + b * 4, 0, 0, 0);
@@ -202,13 +219,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_fp8(
         for (int q = 0; q < 4; q++) issue_part(st, b, q);
     };
 
-    f32x4 acc[4][4];
+    f32x4 acc[4][4 * SH::kHalves];
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 4 * SH::kHalves; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int half = lane >> 4;
+    // One k-block from stage st; the pieces of the DMA into stage nst (k-block
+    // nb) are issued between the first half's MFMA groups.
     auto compute = [&](auto st, auto nst, int nb) {
         constexpr int S = decltype(st)::value;
         const uint8_t* A = stageA(st);
@@ -217,62 +236,72 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_fp8(
         float f[4];
 #pragma unroll
         for (int i = 0; i < 4; i++) f[i] = Ssc[i * 16 + (lane & 15)] * sw[S];
-        i32x8 xf[4], wf[4];
-#pragma unroll
-        for (int j = 0; j < 4; j++) wf[j] = frag(W, wn * 64 + j * 16 + (lane & 15), half);
+        i32x8 xf[4];
 #pragma unroll
         for (int i = 0; i < 4; i++) xf[i] = frag(A, wm * 64 + i * 16 + (lane & 15), half);
-        // Row group i: four MFMAs; their results are promoted while the next
-        // group's MFMAs run (two groups of partials live at a time).
-        f32x4 prev[4];
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            f32x4 cur[4];
+        for (int hh = 0; hh < SH::kHalves; hh++) {
+            i32x8 wf[4];
 #pragma unroll
             for (int j = 0; j < 4; j++)
-                cur[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    wf[j], xf[i], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-            issue_part(nst, nb, i);
-            if (i > 0) {
+                wf[j] = frag(W, wn * SH::kWaveCols + hh * 64 + j * 16 + (lane & 15), half);
+            // Row group i: four MFMAs; their results are promoted while the
+            // next group's MFMAs run (two groups of partials live at a time).
+            f32x4 prev[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                f32x4 cur[4];
 #pragma unroll
                 for (int j = 0; j < 4; j++)
+                    cur[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        wf[j], xf[i], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                if (hh == 0) issue_part(nst, nb, i);
+                if (i > 0) {
 #pragma unroll
-                    for (int r = 0; r < 4; r++)
-                        acc[i - 1][j][r] = fmaf(prev[j][r], f[i - 1], acc[i - 1][j][r]);
+                    for (int j = 0; j < 4; j++)
+#pragma unroll
+                        for (int r = 0; r < 4; r++)
+                            acc[i - 1][hh * 4 + j][r] =
+                                fmaf(prev[j][r], f[i - 1], acc[i - 1][hh * 4 + j][r]);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; j++) prev[j] = cur[j];
+                __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
-            for (int j = 0; j < 4; j++) prev[j] = cur[j];
-            __builtin_amdgcn_sched_barrier(0);
+            for (int j = 0; j < 4; j++)
+#pragma unroll
+                for (int r = 0; r < 4; r++)
+                    acc[3][hh * 4 + j][r] = fmaf(prev[j][r], f[3], acc[3][hh * 4 + j][r]);
         }
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-#pragma unroll
-            for (int r = 0; r < 4; r++) acc[3][j][r] = fmaf(prev[j][r], f[3], acc[3][j][r]);
     };
 
-    // One k-block: its stage's DMA (this wave's part) is complete once at most
-    // the next k-block's operations are in flight; the barrier then makes
-    // every wave's part visible and guarantees that all waves are done with
-    // the stage the new prefetch overwrites (read in the previous step). The
-    // prefetch is always issued, clamped to the last k-block, so the loop has
-    // one shape; the clamped copies land in a stage that is never read.
+    // One k-block: the DMA of its stage (this wave's part) is complete once
+    // at most the loads of the k-blocks after it are in flight (kStages - 2 of
+    // them); the barrier then makes every wave's part visible and guarantees
+    // that all waves are done with the stage the new prefetch overwrites
+    // (read in the previous step). The prefetch is always issued, clamped to
+    // the last k-block, so the loop has one shape; clamped copies land in a
+    // stage that is never read.
+    constexpr int kAhead = kStages - 1;
     auto step = [&](auto st, int b) {
         constexpr int S = decltype(st)::value;
-        wait_vmcnt<kOpsPerStage>();
+        wait_vmcnt<SH::kOps * (kAhead - 1)>();
         lds_barrier();
-        compute(st, std::integral_constant<int, (S + 2) % kStages>{}, min(b + 2, KB - 1));
+        compute(st, std::integral_constant<int, (S + kAhead) % kStages>{}, min(b + kAhead, KB - 1));
     };
 
     issue(std::integral_constant<int, 0>{}, 0);
-    issue(std::integral_constant<int, 1>{}, min(1, KB - 1));
+    if constexpr (kAhead > 1) issue(std::integral_constant<int, 1>{}, min(1, KB - 1));
     int b = 0;
     for (; b + kStages <= KB; b += kStages) {
         step(std::integral_constant<int, 0>{}, b);
         step(std::integral_constant<int, 1>{}, b + 1);
-        step(std::integral_constant<int, 2>{}, b + 2);
+        if constexpr (kStages > 2) step(std::integral_constant<int, 2>{}, b + 2);
     }
     if (b < KB) step(std::integral_constant<int, 0>{}, b);
-    if (b + 1 < KB) step(std::integral_constant<int, 1>{}, b + 1);
+    if constexpr (kStages > 2)
+        if (b + 1 < KB) step(std::integral_constant<int, 1>{}, b + 1);
     // No LDS DMA may still be writing when the workgroup's LDS is released.
     wait_vmcnt<0>();
 
@@ -282,9 +311,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_fp8(
     for (int i = 0; i < 4; i++) {
         const int r = wm * 64 + i * 16 + (lane & 15);
         if (r >= rows) continue;
-        uint16_t* yr = y + (int64_t)(row0 + r) * N + n0 + wn * 64 + 4 * half;
+        uint16_t* yr = y + (int64_t)(row0 + r) * N + n0 + wn * SH::kWaveCols + 4 * half;
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
+        for (int j = 0; j < 4 * SH::kHalves; j++) {
             const uint2 v = make_uint2(pack_bf16x2(acc[i][j][0], acc[i][j][1]),
                                        pack_bf16x2(acc[i][j][2], acc[i][j][3]));
             *reinterpret_cast<uint2*>(yr + j * 16) = v;
@@ -292,9 +321,26 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_fp8(
     }
 }
 
+// One kernel per tile shape (the body is shared).
+__global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_fp8_m128(
+    const uint8_t* __restrict__ a, const float* __restrict__ a_scales,
+    const uint8_t* __restrict__ w, const float* __restrict__ w_scales,
+    const int4* __restrict__ tiles, const int32_t* __restrict__ tile_count,
+    uint16_t* __restrict__ y, int N, int K) {
+    gemm_body<128>(a, a_scales, w, w_scales, tiles, tile_count, y, N, K);
+}
+
+__global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_fp8_m256(
+    const uint8_t* __restrict__ a, const float* __restrict__ a_scales,
+    const uint8_t* __restrict__ w, const float* __restrict__ w_scales,
+    const int4* __restrict__ tiles, const int32_t* __restrict__ tile_count,
+    uint16_t* __restrict__ y, int N, int K) {
+    gemm_body<256>(a, a_scales, w, w_scales, tiles, tile_count, y, N, K);
+}
+
 }  // namespace
 
-int64_t gemm_max_tiles(int64_t max_rows, int E) { return (max_rows + kBM - 1) / kBM + E; }
+int64_t gemm_max_tiles(int64_t max_rows, int E) { return (max_rows + kBMin - 1) / kBMin + E; }
 
 size_t gemm_workspace_bytes(int64_t max_rows, int E) {
     return 256 + (size_t)gemm_max_tiles(max_rows, E) * sizeof(int4);
@@ -305,20 +351,30 @@ hipError_t launch_grouped_gemm_fp8(const void* a, const float* a_scales,
                                    const float* w_scales, int E, int N, int K, int64_t max_rows,
                                    void* y, void* workspace, hipStream_t stream,
                                    LaunchInfo info[2]) {
-    const int64_t max_tiles = gemm_max_tiles(max_rows, E);
+    // 256-row tiles when the capacity allows segments of prefill size (an
+    // expert's last tile is then a small part of its work), else 128.
+    const int bm = max_rows >= 512 * (int64_t)E ? 256 : 128;
+    const int64_t max_tiles = gemm_max_tiles(max_rows, E);   // bounds either height
     int32_t* count = static_cast<int32_t*>(workspace);
     int4* tiles = reinterpret_cast<int4*>(static_cast<char*>(workspace) + 256);
     hipLaunchKernelGGL(k_gemm_tiles, dim3(1), dim3(kTileListThreads), 0, stream, expert_offsets,
-                       E, (int)max_rows, (int)max_tiles, tiles, count);
+                       E, (int)max_rows, (int)max_tiles, bm, tiles, count);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int64_t grid = max_tiles * (N / kBN);
-    hipLaunchKernelGGL(k_grouped_gemm_fp8, dim3((unsigned)grid), dim3(kGemmThreads), 0, stream,
-                       static_cast<const uint8_t*>(a), a_scales, static_cast<const uint8_t*>(w),
-                       w_scales, tiles, count, static_cast<uint16_t*>(y), N, K);
+    const auto* a8 = static_cast<const uint8_t*>(a);
+    const auto* w8 = static_cast<const uint8_t*>(w);
+    auto* y16 = static_cast<uint16_t*>(y);
+    if (bm == 256)
+        k_grouped_gemm_fp8_m256<<<dim3((unsigned)grid), dim3(kGemmThreads), 0, stream>>>(
+            a8, a_scales, w8, w_scales, tiles, count, y16, N, K);
+    else
+        k_grouped_gemm_fp8_m128<<<dim3((unsigned)grid), dim3(kGemmThreads), 0, stream>>>(
+            a8, a_scales, w8, w_scales, tiles, count, y16, N, K);
     if (info) {
         info[0] = LaunchInfo{1, kTileListThreads, 0, 0};
-        info[1] = LaunchInfo{grid, kGemmThreads, 2 * (kBM + kBN) * kBK, kBN};
+        info[1] = LaunchInfo{grid, kGemmThreads,
+                             (size_t)(bm == 256 ? 2 : 3) * (bm + kBN) * kBK, bm};
     }
     return hipGetLastError();
 }

@@ -134,6 +134,26 @@ def test_gemm_exact_intervals_tight_tolerance(E, K, N, seed):
     assert same >= 0.999
 
 
+@pytest.mark.parametrize("counts,N,K,seed", [([600, 450], 512, 512, 0),      # ragged: partial 256-row tiles
+                                              ([1024, 0, 256], 256, 384, 1),  # aligned, an empty expert
+                                              ([513, 1, 700], 768, 256, 2)])
+def test_gemm_256_row_tiles(counts, N, K, seed):
+    """Capacities of at least 512 rows per expert select 256-row tiles."""
+    rng = np.random.default_rng(40 + seed)
+    E = len(counts)
+    off = np.zeros(E + 1, np.int32)
+    off[1:] = np.cumsum(counts)
+    R = max(int(off[E]) + 5, 512 * E)
+    log(f"gemm 256-row tiles: segments {counts}, rows {R}")
+    a = gen_fp8_weight_codes(1, R, K, 50 + seed)[0]
+    a_s = rng.uniform(0.5, 1.5, size=(R, K // 128)).astype(np.float32)
+    w = gen_fp8_weight_codes(E, N, K, 60 + seed)
+    w_s = gen_weight_scales(E, N, K, 60 + seed)
+    g = oracle.grouped_gemm_fp8(a, a_s, off, w, w_s)
+    y = run_gpu(a, a_s, off, w, w_s)
+    check(y, g, off, K)
+
+
 def test_gemm_deep_inner_dimension():
     """K = 16384 (128 k-blocks: many rounds of the three-stage ring)."""
     rng = np.random.default_rng(12)
