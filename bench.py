@@ -657,7 +657,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this path runs on one GPU; multi-GPU runs are not part of it "
-                                   "(see the sharding note in DESIGN.md)", "n_gpus": args.gpus}))
+                                   "(the path shards by tokens; each GPU would run this same step on its own share)", "n_gpus": args.gpus}))
         sys.exit(2)
 
     import torch
