@@ -656,8 +656,9 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this path runs on one GPU; multi-GPU runs are not part of it "
-                                   "(the path shards by tokens; each GPU would run this same step on its own share)", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this path runs on one GPU; multi-GPU runs are not part of "
+                                   "it (the path shards by tokens; each GPU would run this "
+                                   "same step on its own share)", "n_gpus": args.gpus}))
         sys.exit(2)
 
     import torch
