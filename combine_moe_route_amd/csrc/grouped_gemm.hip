@@ -81,7 +81,7 @@ __device__ __forceinline__ int swz(int row, int chunk) {
     return row * kBK + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
-__device__ __forceinline__ i32x8 frag(const uint8_t* s, int row, int half) {
+[[maybe_unused]] __device__ __forceinline__ i32x8 frag(const uint8_t* s, int row, int half) {
     const u32x4 lo = *reinterpret_cast<const u32x4*>(s + swz(row, 2 * half));
     const u32x4 hi = *reinterpret_cast<const u32x4*>(s + swz(row, 2 * half + 1));
     return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
@@ -102,7 +102,9 @@ __device__ __forceinline__ void wait_vmcnt() {
 // k-blocks being prefetched). The memory clobber keeps the compiler from
 // moving LDS accesses across it; completion of the DMA a wave needs is
 // waited for explicitly before it.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+[[maybe_unused]] __device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_barrier" ::: "memory");
+}
 
 // Tile shapes. Both use 8 waves and 256 output columns; the row count picks
 // the rest:
