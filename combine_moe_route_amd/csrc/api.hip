@@ -38,11 +38,11 @@ int64_t max_rows_of(int64_t T, int E, int k, int row_align) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 
-// Row kernels launch one 64-lane wave per (token, 512 bytes of a bf16 row),
-// four waves per block; keep every grid within the 2^31 - 1 block limit.
-bool row_grid_fits(int64_t T, int H) {
-    const int64_t waves_per_token = ((int64_t)H * 2 / 16 + 63) / 64;
-    return T * waves_per_token / 4 + 1 < kInt32Max;
+// True when every kernel of a planned call fits a launch packet.
+bool all_fit(const moe::LaunchInfo* info, int n) {
+    for (int i = 0; i < n; i++)
+        if (!moe::launch_fits(info[i])) return false;
+    return true;
 }
 
 }  // namespace
@@ -57,6 +57,8 @@ int moe_route_topk(const float* logits, int64_t T, int E, int k, int32_t* topk_i
     if (!logits || !topk_idx || !topk_w) return MOE_ENULL;
     if (!aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4)) return MOE_EALIGN;
     moe::LaunchInfo info;
+    (void)moe::launch_route_topk(logits, T, E, k, 0, 0.0f, topk_idx, topk_w, nullptr, &info, false);
+    if (!all_fit(&info, 1)) return MOE_EINVAL;
     const hipError_t e = moe::launch_route_topk(logits, T, E, k, 0, 0.0f, topk_idx, topk_w,
                                                 static_cast<hipStream_t>(stream), &info);
     if (log_enabled()) log_launch("route_topk", info);
@@ -73,6 +75,9 @@ int moe_route_topk_shared(const float* logits, int64_t T, int E, int k, int n_sh
     if (!logits || !topk_idx || !topk_w) return MOE_ENULL;
     if (!aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4)) return MOE_EALIGN;
     moe::LaunchInfo info;
+    (void)moe::launch_route_topk(logits, T, E, k, n_shared, shared_w, topk_idx, topk_w, nullptr, &info,
+                           false);
+    if (!all_fit(&info, 1)) return MOE_EINVAL;
     const hipError_t e = moe::launch_route_topk(logits, T, E, k, n_shared, shared_w, topk_idx,
                                                 topk_w, static_cast<hipStream_t>(stream), &info);
     if (log_enabled()) log_launch("route_topk_shared", info);
@@ -101,11 +106,19 @@ size_t moe_dispatch_workspace_bytes(int64_t T, int E, int k, int groups) {
     return total;
 }
 
-int moe_dispatch(const void* x, const int32_t* topk_idx, int64_t T, int H, int E, int k,
-                 int groups, int row_align, int out_dtype, void* out, float* out_scales,
-                 int32_t* expert_counts, int32_t* expert_offsets, int32_t* group_offsets,
-                 int32_t* row_src, int32_t* dst_row, void* workspace, size_t workspace_bytes,
-                 void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks and launches of a dispatch call. Sizes and options are checked
+// first (MOE_EINVAL, including the launch geometry), then pointers
+// (MOE_ENULL), alignment (MOE_EALIGN) and the workspace size (MOE_ENOSPC);
+// nothing is launched unless every check passes.
+int dispatch_impl(const void* x, const int32_t* topk_idx, int64_t T, int H, int E, int k,
+                  int groups, int row_align, int out_dtype, void* out, float* out_scales,
+                  int32_t* expert_counts, int32_t* expert_offsets, int32_t* group_offsets,
+                  int32_t* row_src, int32_t* dst_row, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream) {
     // sizes and options
     const int64_t max_rows = max_rows_of(T, E, k, row_align);
     if (max_rows < 0) return MOE_EINVAL;
@@ -113,23 +126,6 @@ int moe_dispatch(const void* x, const int32_t* topk_idx, int64_t T, int H, int E
     if (out_dtype != MOE_OUT_BF16 && out_dtype != MOE_OUT_FP8_E4M3) return MOE_EINVAL;
     const bool fp8 = out_dtype == MOE_OUT_FP8_E4M3;
     if (H < 1 || H > 65536 || H % (fp8 ? 128 : 8) != 0) return MOE_EINVAL;
-    if (!row_grid_fits(T, H)) return MOE_EINVAL;
-    // required pointers
-    if (!expert_counts || !expert_offsets) return MOE_ENULL;
-    if (T > 0 && (!x || !topk_idx || !dst_row)) return MOE_ENULL;
-    if (max_rows > 0 && (!out || !row_src)) return MOE_ENULL;
-    if (fp8 && max_rows > 0 && !out_scales) return MOE_ENULL;
-    // alignment
-    if (!aligned(x, 16) || !aligned(out, 16)) return MOE_EALIGN;
-    if (!aligned(topk_idx, 4) || !aligned(expert_counts, 4) || !aligned(expert_offsets, 4) ||
-        !aligned(group_offsets, 4) || !aligned(row_src, 4) || !aligned(dst_row, 4) ||
-        !aligned(workspace, 4) || (fp8 && !aligned(out_scales, 4)))
-        return MOE_EALIGN;
-    // workspace
-    const size_t need = moe_dispatch_workspace_bytes(T, E, k, groups);
-    if (workspace_bytes < need) return MOE_ENOSPC;
-    if (need > 0 && !workspace) return MOE_ENULL;
-
     moe::DispatchArgs a;
     a.x = x;
     a.topk_idx = topk_idx;
@@ -153,7 +149,24 @@ int moe_dispatch(const void* x, const int32_t* topk_idx, int64_t T, int H, int E
     a.tile_rank = reinterpret_cast<int32_t*>(static_cast<unsigned char*>(workspace) + rank_off);
     a.max_rows = max_rows;
     moe::LaunchInfo info[3];
-    const hipError_t e = moe::launch_dispatch(a, static_cast<hipStream_t>(stream), info);
+    (void)moe::launch_dispatch(a, nullptr, info, false);
+    if (!all_fit(info, 3)) return MOE_EINVAL;
+    // required pointers
+    if (!expert_counts || !expert_offsets) return MOE_ENULL;
+    if (T > 0 && (!x || !topk_idx || !dst_row)) return MOE_ENULL;
+    if (max_rows > 0 && (!out || !row_src)) return MOE_ENULL;
+    if (fp8 && max_rows > 0 && !out_scales) return MOE_ENULL;
+    // alignment
+    if (!aligned(x, 16) || !aligned(out, 16)) return MOE_EALIGN;
+    if (!aligned(topk_idx, 4) || !aligned(expert_counts, 4) || !aligned(expert_offsets, 4) ||
+        !aligned(group_offsets, 4) || !aligned(row_src, 4) || !aligned(dst_row, 4) ||
+        !aligned(workspace, 4) || (fp8 && !aligned(out_scales, 4)))
+        return MOE_EALIGN;
+    // workspace
+    if (workspace_bytes < ws_total) return MOE_ENOSPC;
+    if (ws_total > 0 && !workspace) return MOE_ENULL;
+
+    const hipError_t e = moe::launch_dispatch(a, stream, info);
     if (log_enabled()) {
         log_launch("dispatch.tile_hist", info[0]);
         log_launch("dispatch.scan", info[1]);
@@ -162,17 +175,32 @@ int moe_dispatch(const void* x, const int32_t* topk_idx, int64_t T, int H, int E
     return status_of(e);
 }
 
+}  // namespace
+
+extern "C" {
+
+int moe_dispatch(const void* x, const int32_t* topk_idx, int64_t T, int H, int E, int k,
+                 int groups, int row_align, int out_dtype, void* out, float* out_scales,
+                 int32_t* expert_counts, int32_t* expert_offsets, int32_t* group_offsets,
+                 int32_t* row_src, int32_t* dst_row, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+    return dispatch_impl(x, topk_idx, T, H, E, k, groups, row_align, out_dtype, out, out_scales,
+                         expert_counts, expert_offsets, group_offsets, row_src, dst_row,
+                         workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
 int moe_combine(const void* expert_out, const int32_t* dst_row, const float* topk_w, int64_t T,
                 int H, int k, void* y, void* stream) {
     if (T < 0 || k < 1 || k > MOE_MAX_EXPERTS || H < 1 || H > 65536 || H % 8 != 0)
         return MOE_EINVAL;
     if (T > kInt32Max || T * (int64_t)k > kInt32Max) return MOE_EINVAL;
-    if (!row_grid_fits(T, H)) return MOE_EINVAL;
+    moe::LaunchInfo info;
+    (void)moe::launch_combine(expert_out, dst_row, topk_w, T, H, k, y, nullptr, &info, false);
+    if (!all_fit(&info, 1)) return MOE_EINVAL;
     if (T == 0) return MOE_OK;
     if (!expert_out || !dst_row || !topk_w || !y) return MOE_ENULL;
     if (!aligned(expert_out, 16) || !aligned(y, 16)) return MOE_EALIGN;
     if (!aligned(dst_row, 4) || !aligned(topk_w, 4)) return MOE_EALIGN;
-    moe::LaunchInfo info;
     const hipError_t e = moe::launch_combine(expert_out, dst_row, topk_w, T, H, k, y,
                                              static_cast<hipStream_t>(stream), &info);
     if (log_enabled()) log_launch("combine", info);
@@ -186,7 +214,10 @@ int moe_combine_send(const void* expert_out, const int32_t* dst_row, const float
         return MOE_EINVAL;
     if (groups < 1 || groups > E || E % groups != 0) return MOE_EINVAL;
     if (T > kInt32Max || T * (int64_t)k > kInt32Max) return MOE_EINVAL;
-    if (!row_grid_fits(T, H)) return MOE_EINVAL;
+    moe::LaunchInfo info;
+    (void)moe::launch_combine_send(expert_out, dst_row, topk_w, topk_idx, T, H, E, k, groups, partial,
+                             partial_count, nullptr, &info, false);
+    if (!all_fit(&info, 1)) return MOE_EINVAL;
     if (T == 0) return MOE_OK;
     if (!expert_out || !dst_row || !topk_w || !topk_idx || !partial || !partial_count)
         return MOE_ENULL;
@@ -194,7 +225,6 @@ int moe_combine_send(const void* expert_out, const int32_t* dst_row, const float
     if (!aligned(dst_row, 4) || !aligned(topk_w, 4) || !aligned(topk_idx, 4) ||
         !aligned(partial_count, 4))
         return MOE_EALIGN;
-    moe::LaunchInfo info;
     const hipError_t e = moe::launch_combine_send(expert_out, dst_row, topk_w, topk_idx, T, H, E,
                                                   k, groups, partial, partial_count,
                                                   static_cast<hipStream_t>(stream), &info);
@@ -207,12 +237,13 @@ int moe_combine_recv(const void* partial, const int32_t* partial_count, int64_t 
     if (T < 0 || k < 1 || k > MOE_MAX_EXPERTS || H < 1 || H > 65536 || H % 8 != 0)
         return MOE_EINVAL;
     if (T > kInt32Max || T * (int64_t)k > kInt32Max) return MOE_EINVAL;
-    if (!row_grid_fits(T, H)) return MOE_EINVAL;
+    moe::LaunchInfo info;
+    (void)moe::launch_combine_recv(partial, partial_count, T, H, k, y, nullptr, &info, false);
+    if (!all_fit(&info, 1)) return MOE_EINVAL;
     if (T == 0) return MOE_OK;
     if (!partial || !partial_count || !y) return MOE_ENULL;
     if (!aligned(partial, 16) || !aligned(y, 16)) return MOE_EALIGN;
     if (!aligned(partial_count, 4)) return MOE_EALIGN;
-    moe::LaunchInfo info;
     const hipError_t e = moe::launch_combine_recv(partial, partial_count, T, H, k, y,
                                                   static_cast<hipStream_t>(stream), &info);
     if (log_enabled()) log_launch("combine_recv", info);
@@ -248,8 +279,12 @@ int moe_grouped_gemm_fp8(const void* a, const float* a_scales, const int32_t* ex
     if (E < 1 || E > MOE_MAX_EXPERTS || max_rows < 0 || max_rows > kInt32Max) return MOE_EINVAL;
     if (N < 256 || N > (1 << 20) || N % 256 != 0) return MOE_EINVAL;
     if (K < 128 || K > (1 << 20) || K % 128 != 0) return MOE_EINVAL;
-    // One workgroup per (128-row tile, 256 columns); the grid must fit 2^31 - 1.
-    if (moe::gemm_max_tiles(max_rows, E) * (N / 256) >= kInt32Max) return MOE_EINVAL;
+    {
+        moe::LaunchInfo plan[2];
+        (void)moe::launch_grouped_gemm_fp8(nullptr, nullptr, nullptr, nullptr, nullptr, E, N, K,
+                                     max_rows, nullptr, nullptr, nullptr, plan, false);
+        if (!all_fit(plan, 2)) return MOE_EINVAL;
+    }
     if (max_rows == 0) return MOE_OK;
     if (!a || !a_scales || !expert_offsets || !w || !w_scales || !y || !workspace)
         return MOE_ENULL;

@@ -90,13 +90,13 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const uint16_t* __r
 
 hipError_t launch_combine(const void* expert_out, const int32_t* dst_row, const float* topk_w,
                           int64_t T, int H, int k, void* y, hipStream_t stream,
-                          LaunchInfo* info) {
+                          LaunchInfo* info, bool run) {
     const int C = H / 8;
     const int CW = (C + kWave - 1) / kWave;
     const int64_t waves = T * CW;
     const int64_t blocks = (waves + kCombineWaves - 1) / kCombineWaves;
     if (info) *info = LaunchInfo{blocks, kCombineThreads, 0, CW};
-    if (blocks == 0) return hipSuccess;
+    if (!run || blocks == 0) return hipSuccess;
     k_combine<<<dim3((unsigned)blocks), dim3(kCombineThreads), 0, stream>>>(
         static_cast<const uint16_t*>(expert_out), dst_row, topk_w, T, H, k,
         static_cast<uint16_t*>(y));

@@ -158,11 +158,11 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine_recv(
 hipError_t launch_combine_send(const void* expert_out, const int32_t* dst_row,
                                const float* topk_w, const int32_t* topk_idx, int64_t T, int H,
                                int E, int k, int groups, void* partial, int32_t* count,
-                               hipStream_t stream, LaunchInfo* info) {
+                               hipStream_t stream, LaunchInfo* info, bool run) {
     const int CW = (H / 8 + kWave - 1) / kWave;
     const int64_t blocks = (T * CW + kCombineWaves - 1) / kCombineWaves;
     if (info) *info = LaunchInfo{blocks, kCombineThreads, 0, CW};
-    if (blocks == 0) return hipSuccess;
+    if (!run || blocks == 0) return hipSuccess;
     k_combine_send<<<dim3((unsigned)blocks), dim3(kCombineThreads), 0, stream>>>(
         static_cast<const uint16_t*>(expert_out), dst_row, topk_w, topk_idx, T, H, E, k,
         E / groups, static_cast<uint16_t*>(partial), count);
@@ -170,11 +170,12 @@ hipError_t launch_combine_send(const void* expert_out, const int32_t* dst_row,
 }
 
 hipError_t launch_combine_recv(const void* partial, const int32_t* count, int64_t T, int H,
-                               int k, void* y, hipStream_t stream, LaunchInfo* info) {
+                               int k, void* y, hipStream_t stream, LaunchInfo* info,
+                               bool run) {
     const int CW = (H / 8 + kWave - 1) / kWave;
     const int64_t blocks = (T * CW + kCombineWaves - 1) / kCombineWaves;
     if (info) *info = LaunchInfo{blocks, kCombineThreads, 0, CW};
-    if (blocks == 0) return hipSuccess;
+    if (!run || blocks == 0) return hipSuccess;
     k_combine_recv<<<dim3((unsigned)blocks), dim3(kCombineThreads), 0, stream>>>(
         static_cast<const uint16_t*>(partial), count, T, H, k, static_cast<uint16_t*>(y));
     return hipGetLastError();

@@ -418,13 +418,36 @@ __global__ __launch_bounds__(1024) void k_scatter_fp8(
 
 // ---------------------------------------------------------------- launch
 
-hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream, LaunchInfo info[3]) {
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream, LaunchInfo info[3],
+                           bool run) {
     const int64_t tiles = dispatch_tiles(a.T);
     hipError_t err;
 
-    // K2
+    // geometry of the three kernels first
     const size_t hist_lds = (size_t)kHistWaves * a.E * (sizeof(uint64_t) + sizeof(int32_t));
-    if (info) info[0] = LaunchInfo{tiles, kTileTokens, hist_lds, 0};
+    int pad_per_expert = 0, pad_rows_per_block = 0;
+    if (a.row_align > 1 && a.T > 0) {
+        pad_per_expert = a.row_align - 1 < 4 ? a.row_align - 1 : 4;
+        pad_rows_per_block = (a.row_align - 1 + pad_per_expert - 1) / pad_per_expert;
+    }
+    const int64_t pad_blocks = (int64_t)a.E * pad_per_expert;
+    int fp8_waves = (a.H / 16 + kWave - 1) / kWave;
+    if (fp8_waves > 16) fp8_waves = 16;
+    const int fp8_threads = fp8_waves * kWave > kScatterThreads ? fp8_waves * kWave : kScatterThreads;
+    const int64_t bf16_waves_per_token = (a.H / 8 + kWave - 1) / kWave;
+    const int64_t scatter_blocks =
+        a.fp8 ? pad_blocks + a.T
+              : pad_blocks + (a.T * bf16_waves_per_token + kScatterWaves - 1) / kScatterWaves;
+    if (info) {
+        info[0] = LaunchInfo{tiles, kTileTokens, hist_lds, 0};
+        info[1] = LaunchInfo{1, kScanThreads, 0, 0};
+        info[2] = a.fp8 ? LaunchInfo{scatter_blocks, fp8_threads,
+                                     (size_t)(a.H / 128) * sizeof(float), fp8_waves}
+                        : LaunchInfo{scatter_blocks, kScatterThreads, 0, bf16_waves_per_token};
+    }
+    if (!run) return hipSuccess;
+
+    // K2
     if (tiles > 0) {
         k_tile_hist<<<dim3((unsigned)tiles), dim3(kTileTokens), hist_lds, stream>>>(
             a.topk_idx, a.T, a.E, a.k, a.tile_counts, a.tile_rank);
@@ -432,42 +455,24 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream, LaunchInfo
     }
 
     // K3
-    if (info) info[1] = LaunchInfo{1, kScanThreads, 0, 0};
     k_scan<<<1, kScanThreads, 0, stream>>>(a.tile_counts, tiles, a.E, a.row_align, a.groups,
                                             a.expert_counts, a.expert_offsets, a.group_offsets);
     if ((err = hipGetLastError()) != hipSuccess) return err;
 
     // K4: leading blocks zero pad rows, then the token work
-    int pad_per_expert = 0, pad_rows_per_block = 0;
-    if (a.row_align > 1 && a.T > 0) {
-        pad_per_expert = a.row_align - 1 < 4 ? a.row_align - 1 : 4;
-        pad_rows_per_block = (a.row_align - 1 + pad_per_expert - 1) / pad_per_expert;
-    }
-    const int64_t pad_blocks = (int64_t)a.E * pad_per_expert;
     unsigned char* out = static_cast<unsigned char*>(a.out);
     const uint16_t* x = static_cast<const uint16_t*>(a.x);
     if (a.fp8) {
         // one block per token, one wave per 64-unit chunk (at most 16 waves)
-        const int units = a.H / 16;
-        int waves = (units + kWave - 1) / kWave;
-        if (waves > 16) waves = 16;
-        const int64_t blocks = pad_blocks + a.T;
-        const int threads = waves * kWave > kScatterThreads ? waves * kWave : kScatterThreads;
         const size_t lds = (size_t)(a.H / 128) * sizeof(float);
-        if (info) info[2] = LaunchInfo{blocks, threads, lds, waves};
-        if (blocks == 0) return hipSuccess;
-        k_scatter_fp8<<<dim3((unsigned)blocks), dim3(threads), lds, stream>>>(
+        if (scatter_blocks == 0) return hipSuccess;
+        k_scatter_fp8<<<dim3((unsigned)scatter_blocks), dim3(fp8_threads), lds, stream>>>(
             x, a.topk_idx, a.tile_rank, a.tile_counts, a.expert_counts, a.expert_offsets, a.T,
             a.H, a.E, a.k, a.max_rows, (int)pad_blocks, pad_per_expert, pad_rows_per_block, out,
             a.out_scales, a.row_src, a.dst_row);
     } else {
-        const int units = a.H / 8;
-        const int64_t waves_per_token = (units + kWave - 1) / kWave;
-        const int64_t blocks =
-            pad_blocks + (a.T * waves_per_token + kScatterWaves - 1) / kScatterWaves;
-        if (info) info[2] = LaunchInfo{blocks, kScatterThreads, 0, waves_per_token};
-        if (blocks == 0) return hipSuccess;
-        k_scatter_bf16<<<dim3((unsigned)blocks), dim3(kScatterThreads), 0, stream>>>(
+        if (scatter_blocks == 0) return hipSuccess;
+        k_scatter_bf16<<<dim3((unsigned)scatter_blocks), dim3(kScatterThreads), 0, stream>>>(
             x, a.topk_idx, a.tile_rank, a.tile_counts, a.expert_counts, a.expert_offsets, a.T,
             a.H, a.E, a.k, a.max_rows, (int)pad_blocks, pad_per_expert, pad_rows_per_block, out,
             a.row_src, a.dst_row);

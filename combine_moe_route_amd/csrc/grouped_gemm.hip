@@ -352,18 +352,24 @@ hipError_t launch_grouped_gemm_fp8(const void* a, const float* a_scales,
                                    const int32_t* expert_offsets, const void* w,
                                    const float* w_scales, int E, int N, int K, int64_t max_rows,
                                    void* y, void* workspace, hipStream_t stream,
-                                   LaunchInfo info[2]) {
+                                   LaunchInfo info[2], bool run) {
     // 256-row tiles when the capacity allows segments of prefill size (an
     // expert's last tile is then a small part of its work), else 128.
     const int bm = max_rows >= 512 * (int64_t)E ? 256 : 128;
     const int64_t max_tiles = gemm_max_tiles(max_rows, E);   // bounds either height
+    const int64_t grid = max_tiles * (N / kBN);
+    if (info) {
+        info[0] = LaunchInfo{1, kTileListThreads, 0, 0};
+        info[1] = LaunchInfo{grid, kGemmThreads,
+                             (size_t)(bm == 256 ? 2 : 3) * (bm + kBN) * kBK, bm};
+    }
+    if (!run) return hipSuccess;
     int32_t* count = static_cast<int32_t*>(workspace);
     int4* tiles = reinterpret_cast<int4*>(static_cast<char*>(workspace) + 256);
     hipLaunchKernelGGL(k_gemm_tiles, dim3(1), dim3(kTileListThreads), 0, stream, expert_offsets,
                        E, (int)max_rows, (int)max_tiles, bm, tiles, count);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const int64_t grid = max_tiles * (N / kBN);
     const auto* a8 = static_cast<const uint8_t*>(a);
     const auto* w8 = static_cast<const uint8_t*>(w);
     auto* y16 = static_cast<uint16_t*>(y);
@@ -373,11 +379,6 @@ hipError_t launch_grouped_gemm_fp8(const void* a, const float* a_scales,
     else
         k_grouped_gemm_fp8_m128<<<dim3((unsigned)grid), dim3(kGemmThreads), 0, stream>>>(
             a8, a_scales, w8, w_scales, tiles, count, y16, N, K);
-    if (info) {
-        info[0] = LaunchInfo{1, kTileListThreads, 0, 0};
-        info[1] = LaunchInfo{grid, kGemmThreads,
-                             (size_t)(bm == 256 ? 2 : 3) * (bm + kBN) * kBK, bm};
-    }
     return hipGetLastError();
 }
 

@@ -18,9 +18,20 @@ struct LaunchInfo {
     int64_t param = 0;   // kernel-specific: lanes per token, tokens per block, ...
 };
 
+// A launch packet counts work-items in 32 bits (grid_size_x) and blocks in
+// 31: a kernel fits when blocks * threads < 2^32 and blocks < 2^31.
+inline bool launch_fits(const LaunchInfo& i) {
+    return i.grid >= 0 && i.grid < ((int64_t)1 << 31) &&
+           i.grid * (int64_t)i.block < ((int64_t)1 << 32);
+}
+
+// Every launcher below fills `info` (one entry per kernel it enqueues, in
+// order) before launching anything; with run == false it only fills `info`,
+// so callers can check the geometry of a whole call before the first launch.
+
 hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k, int n_shared,
                              float shared_w, int32_t* topk_idx, float* topk_w,
-                             hipStream_t stream, LaunchInfo* info);
+                             hipStream_t stream, LaunchInfo* info, bool run = true);
 
 hipError_t launch_route_replicas(int32_t* topk_idx, int64_t T, int k, int E,
                                  const int32_t* replica_base, hipStream_t stream);
@@ -49,19 +60,21 @@ int64_t dispatch_tiles(int64_t T);
 // ranks [T, k]. Returns the byte offset of the ranks; *total gets the size.
 size_t dispatch_workspace_layout(int64_t T, int E, int k, size_t* total);
 
-hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream, LaunchInfo info[3]);
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream, LaunchInfo info[3],
+                           bool run = true);
 
 hipError_t launch_combine(const void* expert_out, const int32_t* dst_row, const float* topk_w,
                           int64_t T, int H, int k, void* y, hipStream_t stream,
-                          LaunchInfo* info);
+                          LaunchInfo* info, bool run = true);
 
 hipError_t launch_combine_send(const void* expert_out, const int32_t* dst_row,
                                const float* topk_w, const int32_t* topk_idx, int64_t T, int H,
                                int E, int k, int groups, void* partial, int32_t* count,
-                               hipStream_t stream, LaunchInfo* info);
+                               hipStream_t stream, LaunchInfo* info, bool run = true);
 
 hipError_t launch_combine_recv(const void* partial, const int32_t* count, int64_t T, int H,
-                               int k, void* y, hipStream_t stream, LaunchInfo* info);
+                               int k, void* y, hipStream_t stream, LaunchInfo* info,
+                               bool run = true);
 
 hipError_t launch_expert_scale(const void* disp, const float* disp_scales,
                                const int32_t* row_src, const int32_t* topk_idx,
@@ -76,6 +89,6 @@ hipError_t launch_grouped_gemm_fp8(const void* a, const float* a_scales,
                                    const int32_t* expert_offsets, const void* w,
                                    const float* w_scales, int E, int N, int K, int64_t max_rows,
                                    void* y, void* workspace, hipStream_t stream,
-                                   LaunchInfo info[2]);
+                                   LaunchInfo info[2], bool run = true);
 
 }  // namespace moe

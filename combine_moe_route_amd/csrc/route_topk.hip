@@ -232,7 +232,7 @@ static void launch_s(const RouteArgs& a, hipStream_t stream, int64_t blocks) {
 
 hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k, int n_shared,
                              float shared_w, int32_t* topk_idx, float* topk_w,
-                             hipStream_t stream, LaunchInfo* info) {
+                             hipStream_t stream, LaunchInfo* info, bool run) {
     int S = 1;
     while (S < E && S < kWave) S <<= 1;
     const int nv = (E + S - 1) / S;
@@ -240,7 +240,7 @@ hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k, int n
     const int64_t tokens_per_block = (threads / kWave) * (kWave / S);
     const int64_t blocks = (T + tokens_per_block - 1) / tokens_per_block;
     if (info) *info = LaunchInfo{blocks, threads, 0, S};
-    if (blocks == 0) return hipSuccess;
+    if (!run || blocks == 0) return hipSuccess;
     const RouteArgs a{logits, T, E, k, k + n_shared, n_shared, shared_w, topk_idx, topk_w};
     switch (S) {
         case 1: launch_s<1, 1>(a, stream, blocks); break;

@@ -22,7 +22,10 @@
  *
  * Error behaviour: every function returns a moe_status. All argument checks
  * run on the host before any HIP call, so an invalid call launches nothing
- * and needs no GPU. MOE_EHIP reports a launch failure; faults inside kernels
+ * and needs no GPU. Among them: every kernel a call would enqueue must fit
+ * one launch packet, i.e. its blocks times threads per block stay below 2^32
+ * work-items (the packet's grid size is a 32-bit count of work-items), else
+ * the call returns MOE_EINVAL before its first launch. MOE_EHIP reports a launch failure; faults inside kernels
  * surface at the caller's next synchronisation. Values are not validated:
  * logits must be finite, and each token's expert ids must be distinct.
  * Calls on one stream are ordered; calls that share a workspace must not run
@@ -128,8 +131,10 @@ size_t moe_dispatch_workspace_bytes(int64_t T, int E, int k, int groups);
  *   topk_idx       device, int32 [T, k]; an id outside [0, E) drops that slot
  *                  (not counted, dst_row = -1, no row written)
  *   T, H, E, k     1 <= k <= E <= MOE_MAX_EXPERTS; H % 8 == 0 (bf16) or
- *                  H % 128 == 0 (FP8); 1 <= H <= 65536; T * k < 2^31 and
- *                  T * ceil(H / 256) < 2^33 (launch-grid limit)
+ *                  H % 128 == 0 (FP8); 1 <= H <= 65536; T * k < 2^31; the
+ *                  row kernel must fit a launch packet: 64 * T *
+ *                  ceil(H / 512) < 2^32 for bf16 rows, T * 256 < 2^32 for FP8
+ *                  rows up to H = 4096 (up to 1024 threads per token above)
  *   groups         destination groups (1 = none), E % groups == 0; group g
  *                  holds experts [g*E/groups, (g+1)*E/groups), so its rows
  *                  form one contiguous send buffer
@@ -175,7 +180,8 @@ int moe_dispatch(const void* x, const int32_t* topk_idx,
  *   topk_w      device fp32 [T, k]
  *   y           device bf16 [T, H] out, 16-byte aligned
  *   H % 8 == 0, 1 <= H <= 65536, 1 <= k <= MOE_MAX_EXPERTS, T >= 0,
- *   T * k < 2^31, T * ceil(H / 256) < 2^33 (launch-grid limit).
+ *   T * k < 2^31, 64 * T * ceil(H / 512) < 2^32 (one 64-lane wave per token
+ *   and 512 columns must fit a launch packet).
  */
 int moe_combine(const void* expert_out, const int32_t* dst_row,
                 const float* topk_w, int64_t T, int H, int k,

@@ -74,6 +74,7 @@ def test_route_topk_validation():
     assert route(E=1025, k=2) == EINVAL
     assert route(T=-1) == EINVAL
     assert route(T=2 ** 31, k=2) == EINVAL
+    assert route(T=2 ** 27, E=256, k=8) == EINVAL        # one wave per token: 2^33 work-items
     assert route(logits=None) == ENULL
     assert route(idx=None) == ENULL
     assert route(logits=A + 2) == EALIGN
@@ -126,6 +127,15 @@ def test_dispatch_validation():
     assert dispatch(T=-5) == EINVAL
     assert dispatch(T=2 ** 29, k=8) == EINVAL            # rows overflow int32
     assert dispatch(T=2 ** 27, H=65536, k=1, E=1) == EINVAL   # launch grid too large
+    # every kernel must fit a launch packet (blocks * threads < 2^32): bf16
+    # rows of 7168 take 14 waves per token, so 5M tokens need 4.48G
+    # work-items in the scatter; rejected before any launch, even with a
+    # workspace too small (sizes are checked first)
+    big = dict(T=5_000_000, H=7168, k=1, E=1, wsb=1 << 40)
+    assert dispatch(**big) == EINVAL
+    assert dispatch(**dict(big, wsb=16)) == EINVAL
+    assert dispatch(**dict(big, T=4_000_000, wsb=16)) == ENOSPC   # 3.58G work-items fit
+    assert dispatch(T=20_000_000, H=1024, k=1, E=1, dt=1, wsb=1 << 40) == EINVAL  # FP8: T blocks x 256
     assert dispatch(x=None) == ENULL
     assert dispatch(idx=None) == ENULL
     assert dispatch(out=None) == ENULL
@@ -152,6 +162,8 @@ def test_combine_validation():
     assert c(k=1025) == EINVAL
     assert c(T=-1) == EINVAL
     assert c(T=2 ** 28, H=65536, k=1) == EINVAL          # launch grid too large
+    assert c(T=5_000_000, H=7168, k=1) == EINVAL         # 4.48G work-items
+    assert c(T=4_000_000, H=7168, k=1, y=None) == ENULL  # fits; fails later on the pointer
     assert c(eo=None) == ENULL
     assert c(y=None) == ENULL
     assert c(eo=A + 8) == EALIGN
