@@ -18,6 +18,7 @@ _API = (
     "moe_combine_send",
     "moe_dispatch",
     "moe_dispatch_max_rows",
+    "moe_dispatch_no_alloc",
     "moe_dispatch_workspace_bytes",
     "moe_grouped_gemm_fp8",
     "moe_grouped_gemm_workspace_bytes",

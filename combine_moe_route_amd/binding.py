@@ -21,6 +21,7 @@ LIB_PATH = os.environ.get("MOE_ROUTE_LIB", os.path.join(_HERE, "libmoeroute.so")
 MOE_OK, MOE_EINVAL, MOE_ENOSPC, MOE_EALIGN, MOE_EHIP, MOE_ENULL = 0, -1, -2, -3, -4, -5
 MOE_OUT_BF16, MOE_OUT_FP8_E4M3 = 0, 1
 MOE_MAX_EXPERTS = 1024
+MOE_NO_ALLOC_SCRATCH_BYTES = 16 << 20
 
 # every symbol include/moe_route.h declares
 EXPORTS = (
@@ -30,6 +31,7 @@ EXPORTS = (
     "moe_dispatch_max_rows",
     "moe_dispatch_workspace_bytes",
     "moe_dispatch",
+    "moe_dispatch_no_alloc",
     "moe_combine",
     "moe_combine_send",
     "moe_combine_recv",
@@ -66,6 +68,9 @@ def _load() -> ctypes.CDLL:
     lib.moe_dispatch.argtypes = [P, P, i64, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P,
                                  P, ctypes.c_size_t, P]
     lib.moe_dispatch.restype = i32
+    lib.moe_dispatch_no_alloc.argtypes = [P, P, i64, i32, i32, i32, i32, i32, i32, P, P, P, P, P,
+                                          P, P, P]
+    lib.moe_dispatch_no_alloc.restype = i32
     lib.moe_combine.argtypes = [P, P, P, i64, i32, i32, P, P]
     lib.moe_combine.restype = i32
     lib.moe_combine_send.argtypes = [P, P, P, P, i64, i32, i32, i32, i32, P, P, P]
@@ -193,11 +198,12 @@ class DispatchBuffers(NamedTuple):
 
 
 def alloc_dispatch(T: int, H: int, E: int, k: int, groups: int = 1, row_align: int = 1,
-                   fp8: bool = False, device="cuda") -> DispatchBuffers:
-    """Capacity-sized output buffers and workspace for moe_dispatch."""
+                   fp8: bool = False, device="cuda", workspace: bool = True) -> DispatchBuffers:
+    """Capacity-sized output buffers and workspace for moe_dispatch (a 4-byte
+    placeholder workspace when `workspace` is false, for moe_dispatch_no_alloc)."""
     dev = torch.device(device)
     R = moe_dispatch_max_rows(T, E, k, row_align)
-    ws = max(moe_dispatch_workspace_bytes(T, E, k, groups), 4)
+    ws = max(moe_dispatch_workspace_bytes(T, E, k, groups), 4) if workspace else 4
     return DispatchBuffers(
         out=torch.empty((R, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev),
         out_scales=torch.empty((R, H // 128), dtype=torch.float32, device=dev) if fp8 else None,
@@ -239,6 +245,39 @@ def moe_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, E: int, groups: int = 
         _ptr(bufs.out_scales) if fp8 else None, _ptr(bufs.expert_counts),
         _ptr(bufs.expert_offsets), _ptr(bufs.group_offsets), _ptr(bufs.row_src),
         _ptr(bufs.dst_row), _ptr(bufs.workspace), bufs.workspace.numel(), _stream(dev)))
+    return bufs
+
+
+def moe_dispatch_no_alloc(x: torch.Tensor, topk_idx: torch.Tensor, E: int, groups: int = 1,
+                          row_align: int = 1, fp8: bool = False,
+                          bufs: Optional[DispatchBuffers] = None) -> DispatchBuffers:
+    """moe_dispatch on the library's own scratch (no workspace argument); the
+    returned buffers' workspace field is an unused placeholder."""
+    _need(x, "x", torch.bfloat16)
+    T, H = x.shape
+    dev = x.device
+    _need(topk_idx, "topk_idx", torch.int32, None, dev)
+    if topk_idx.dim() != 2 or topk_idx.shape[0] != T:
+        raise ValueError(f"topk_idx: shape {tuple(topk_idx.shape)}, expected ({T}, k)")
+    k = topk_idx.shape[1]
+    if bufs is None:
+        bufs = alloc_dispatch(T, H, E, k, groups, row_align, fp8, dev, workspace=False)
+    R = moe_dispatch_max_rows(T, E, k, row_align)
+    _need(bufs.out, "out", torch.uint8 if fp8 else torch.bfloat16, (R, H), dev)
+    if fp8:
+        _need(bufs.out_scales, "out_scales", torch.float32, (R, H // 128), dev)
+    _need(bufs.expert_counts, "expert_counts", torch.int32, (E,), dev)
+    _need(bufs.expert_offsets, "expert_offsets", torch.int32, (E + 1,), dev)
+    _need(bufs.group_offsets, "group_offsets", torch.int32, (groups + 1,), dev)
+    _need(bufs.row_src, "row_src", torch.int32, (R,), dev)
+    _need(bufs.dst_row, "dst_row", torch.int32, (T, k), dev)
+    with torch.cuda.device(dev):   # the library's scratch is per current device
+        _check("moe_dispatch_no_alloc", lib.moe_dispatch_no_alloc(
+            _ptr(x), _ptr(topk_idx), T, H, E, k, groups, row_align,
+            MOE_OUT_FP8_E4M3 if fp8 else MOE_OUT_BF16, _ptr(bufs.out),
+            _ptr(bufs.out_scales) if fp8 else None, _ptr(bufs.expert_counts),
+            _ptr(bufs.expert_offsets), _ptr(bufs.group_offsets), _ptr(bufs.row_src),
+            _ptr(bufs.dst_row), _stream(dev)))
     return bufs
 
 

@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "../../include/moe_route.h"
 #include "launch.h"
 
@@ -113,12 +115,14 @@ namespace {
 // Checks and launches of a dispatch call. Sizes and options are checked
 // first (MOE_EINVAL, including the launch geometry), then pointers
 // (MOE_ENULL), alignment (MOE_EALIGN) and the workspace size (MOE_ENOSPC);
-// nothing is launched unless every check passes.
+// nothing is launched unless every check passes. With library_ws the
+// workspace is the library's own scratch (only its size is checked); with
+// run == false the checks run and nothing is launched.
 int dispatch_impl(const void* x, const int32_t* topk_idx, int64_t T, int H, int E, int k,
                   int groups, int row_align, int out_dtype, void* out, float* out_scales,
                   int32_t* expert_counts, int32_t* expert_offsets, int32_t* group_offsets,
                   int32_t* row_src, int32_t* dst_row, void* workspace, size_t workspace_bytes,
-                  hipStream_t stream) {
+                  hipStream_t stream, bool library_ws = false, bool run = true) {
     // sizes and options
     const int64_t max_rows = max_rows_of(T, E, k, row_align);
     if (max_rows < 0) return MOE_EINVAL;
@@ -164,7 +168,8 @@ int dispatch_impl(const void* x, const int32_t* topk_idx, int64_t T, int H, int 
         return MOE_EALIGN;
     // workspace
     if (workspace_bytes < ws_total) return MOE_ENOSPC;
-    if (ws_total > 0 && !workspace) return MOE_ENULL;
+    if (!library_ws && ws_total > 0 && !workspace) return MOE_ENULL;
+    if (!run) return MOE_OK;
 
     const hipError_t e = moe::launch_dispatch(a, stream, info);
     if (log_enabled()) {
@@ -187,6 +192,60 @@ int moe_dispatch(const void* x, const int32_t* topk_idx, int64_t T, int H, int E
     return dispatch_impl(x, topk_idx, T, H, E, k, groups, row_align, out_dtype, out, out_scales,
                          expert_counts, expert_offsets, group_offsets, row_src, dst_row,
                          workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- no-alloc dispatch
+//
+// Scratch of moe_dispatch_no_alloc: one array per GPU, resident for the life
+// of the process. In host code `scratch` names a host-side stand-in, not the
+// device array, so its address is looked up once per device with
+// hipGetSymbolAddress and only that pointer is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[MOE_NO_ALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the
+// first call on that device), or nullptr on a HIP error.
+void* device_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_dispatch_no_alloc(const void* x, const int32_t* topk_idx, int64_t T, int H, int E, int k,
+                          int groups, int row_align, int out_dtype, void* out, float* out_scales,
+                          int32_t* expert_counts, int32_t* expert_offsets,
+                          int32_t* group_offsets, int32_t* row_src, int32_t* dst_row,
+                          void* stream) {
+    // every check first, with no HIP call (a request needing more scratch
+    // than the array holds fails here with MOE_ENOSPC)
+    const int st = dispatch_impl(x, topk_idx, T, H, E, k, groups, row_align, out_dtype, out,
+                                 out_scales, expert_counts, expert_offsets, group_offsets, row_src,
+                                 dst_row, nullptr, MOE_NO_ALLOC_SCRATCH_BYTES, nullptr,
+                                 /*library_ws=*/true, /*run=*/false);
+    if (st != MOE_OK) return st;
+    void* ws = device_scratch();
+    if (!ws) return MOE_EHIP;
+    return dispatch_impl(x, topk_idx, T, H, E, k, groups, row_align, out_dtype, out, out_scales,
+                         expert_counts, expert_offsets, group_offsets, row_src, dst_row, ws,
+                         MOE_NO_ALLOC_SCRATCH_BYTES, static_cast<hipStream_t>(stream),
+                         /*library_ws=*/true);
 }
 
 int moe_combine(const void* expert_out, const int32_t* dst_row, const float* topk_w, int64_t T,

@@ -166,6 +166,32 @@ int moe_dispatch(const void* x, const int32_t* topk_idx,
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * moe_dispatch for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * call and results without a workspace argument. Its workspace is a static
+ * device array of MOE_NO_ALLOC_SCRATCH_BYTES inside the library, one per
+ * GPU, resident until the process ends; the call allocates nothing (no
+ * hipMalloc, no allocating library routine). Its address is looked up once
+ * per device, on the first call made with that device current.
+ *   Arguments, limits and outputs as for moe_dispatch.
+ *   Returns MOE_ENOSPC, before any HIP call, when the call needs more than
+ *   MOE_NO_ALLOC_SCRATCH_BYTES of workspace (moe_dispatch_workspace_bytes).
+ *   MOE_EHIP if the scratch address cannot be obtained or a launch fails.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (concurrent streams, or with a graph replay holding such a call) race
+ * and give undefined results. Calls ordered on one stream are safe; each
+ * call rewrites what it reads of the array before reading it.
+ */
+#define MOE_NO_ALLOC_SCRATCH_BYTES (16u << 20)
+
+int moe_dispatch_no_alloc(const void* x, const int32_t* topk_idx,
+                          int64_t T, int H, int E, int k, int groups, int row_align,
+                          int out_dtype, void* out, float* out_scales,
+                          int32_t* expert_counts, int32_t* expert_offsets,
+                          int32_t* group_offsets, int32_t* row_src, int32_t* dst_row,
+                          void* stream);
+
+/*
  * Combine: each token's output is the weighted sum of the rows its experts
  * produced, y[t] = bf16(sum_j topk_w[t,j] * expert_out[dst_row[t,j]]),
  * accumulated in fp32 in slot order and rounded once to bf16 (nearest even).

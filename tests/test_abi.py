@@ -153,6 +153,35 @@ def test_dispatch_validation():
     assert dispatch(wsb=lib.moe_dispatch_workspace_bytes(256, 8, 2, 1) - 4) == ENOSPC
 
 
+def test_dispatch_no_alloc_validation():
+    """The no-alloc variant checks everything before any HIP call; a request
+    needing more scratch than the library's array holds is MOE_ENOSPC."""
+    cap = binding.MOE_NO_ALLOC_SCRATCH_BYTES
+    assert cap == 16 << 20
+    assert re.search(r"MOE_NO_ALLOC_SCRATCH_BYTES\s+\(16u << 20\)", open(HEADER).read())
+
+    def na(**kw):
+        a = dict(x=A, idx=B, T=256, H=256, E=8, k=2, groups=1, row_align=1, dt=0,
+                 out=A + 2 ** 20, scales=A + 2 ** 21, counts=B + 2 ** 20,
+                 offsets=B + 2 ** 20 + 64, goff=B + 2 ** 20 + 128, row_src=B + 2 ** 21,
+                 dst_row=B + 2 ** 22)
+        a.update(kw)
+        return lib.moe_dispatch_no_alloc(a["x"], a["idx"], a["T"], a["H"], a["E"], a["k"],
+                                         a["groups"], a["row_align"], a["dt"], a["out"],
+                                         a["scales"], a["counts"], a["offsets"], a["goff"],
+                                         a["row_src"], a["dst_row"], None)
+    assert na(k=0) == EINVAL
+    assert na(groups=3) == EINVAL
+    assert na(H=12) == EINVAL
+    assert na(x=None) == ENULL
+    assert na(out=A + 2 ** 20 + 4) == EALIGN
+    # workspace needed beyond the static scratch
+    T_big = 600_000
+    assert lib.moe_dispatch_workspace_bytes(T_big, 8, 8, 1) > cap
+    assert na(T=T_big, E=8, k=8) == ENOSPC
+    assert lib.moe_dispatch_workspace_bytes(16384, 256, 8, 32) <= cap
+
+
 def test_combine_validation():
     c = lambda eo=A, dr=B, w=B + 4096, T=16, H=64, k=2, y=A + 2 ** 20: lib.moe_combine(
         eo, dr, w, T, H, k, y, None)
