@@ -23,6 +23,7 @@ _API = (
     "moe_grouped_gemm_fp8",
     "moe_grouped_gemm_workspace_bytes",
     "moe_harness_expert_scale",
+    "moe_route_dispatch",
     "moe_route_replicas",
     "moe_route_topk",
     "moe_route_topk_shared",

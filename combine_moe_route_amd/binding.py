@@ -32,6 +32,7 @@ EXPORTS = (
     "moe_dispatch_workspace_bytes",
     "moe_dispatch",
     "moe_dispatch_no_alloc",
+    "moe_route_dispatch",
     "moe_combine",
     "moe_combine_send",
     "moe_combine_recv",
@@ -71,6 +72,9 @@ def _load() -> ctypes.CDLL:
     lib.moe_dispatch_no_alloc.argtypes = [P, P, i64, i32, i32, i32, i32, i32, i32, P, P, P, P, P,
                                           P, P, P]
     lib.moe_dispatch_no_alloc.restype = i32
+    lib.moe_route_dispatch.argtypes = [P, P, i64, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P,
+                                       P, P, P, P, ctypes.c_size_t, P]
+    lib.moe_route_dispatch.restype = i32
     lib.moe_combine.argtypes = [P, P, P, i64, i32, i32, P, P]
     lib.moe_combine.restype = i32
     lib.moe_combine_send.argtypes = [P, P, P, P, i64, i32, i32, i32, i32, P, P, P]
@@ -199,8 +203,10 @@ class DispatchBuffers(NamedTuple):
 
 def alloc_dispatch(T: int, H: int, E: int, k: int, groups: int = 1, row_align: int = 1,
                    fp8: bool = False, device="cuda", workspace: bool = True) -> DispatchBuffers:
-    """Capacity-sized output buffers and workspace for moe_dispatch (a 4-byte
-    placeholder workspace when `workspace` is false, for moe_dispatch_no_alloc)."""
+    """Capacity-sized output buffers and workspace for moe_dispatch and
+    moe_route_dispatch (the workspace zero-filled, as the library requires
+    before its first use; a 4-byte placeholder when `workspace` is false, for
+    moe_dispatch_no_alloc)."""
     dev = torch.device(device)
     R = moe_dispatch_max_rows(T, E, k, row_align)
     ws = max(moe_dispatch_workspace_bytes(T, E, k, groups), 4) if workspace else 4
@@ -212,7 +218,7 @@ def alloc_dispatch(T: int, H: int, E: int, k: int, groups: int = 1, row_align: i
         group_offsets=torch.empty(groups + 1, dtype=torch.int32, device=dev),
         row_src=torch.empty(R, dtype=torch.int32, device=dev),
         dst_row=torch.empty((T, k), dtype=torch.int32, device=dev),
-        workspace=torch.empty(ws, dtype=torch.uint8, device=dev),
+        workspace=torch.zeros(ws, dtype=torch.uint8, device=dev),
     )
 
 
@@ -246,6 +252,48 @@ def moe_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, E: int, groups: int = 
         _ptr(bufs.expert_offsets), _ptr(bufs.group_offsets), _ptr(bufs.row_src),
         _ptr(bufs.dst_row), _ptr(bufs.workspace), bufs.workspace.numel(), _stream(dev)))
     return bufs
+
+
+def moe_route_dispatch(logits: torch.Tensor, x: torch.Tensor, k: int, groups: int = 1,
+                       row_align: int = 1, fp8: bool = False,
+                       bufs: Optional[DispatchBuffers] = None,
+                       topk_idx: Optional[torch.Tensor] = None,
+                       topk_w: Optional[torch.Tensor] = None):
+    """Routing and dispatch in one call: (topk_idx int32 [T,k], topk_w float32
+    [T,k], DispatchBuffers), the same results as moe_route_topk followed by
+    moe_dispatch."""
+    _need(logits, "logits", torch.float32)
+    T, E = logits.shape
+    dev = logits.device
+    _need(x, "x", torch.bfloat16, None, dev)
+    if x.dim() != 2 or x.shape[0] != T:
+        raise ValueError(f"x: shape {tuple(x.shape)}, expected ({T}, H)")
+    H = x.shape[1]
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _need(topk_idx, "topk_idx", torch.int32, (T, k), dev)
+    _need(topk_w, "topk_w", torch.float32, (T, k), dev)
+    if bufs is None:
+        bufs = alloc_dispatch(T, H, E, k, groups, row_align, fp8, dev)
+    R = moe_dispatch_max_rows(T, E, k, row_align)
+    _need(bufs.out, "out", torch.uint8 if fp8 else torch.bfloat16, (R, H), dev)
+    if fp8:
+        _need(bufs.out_scales, "out_scales", torch.float32, (R, H // 128), dev)
+    _need(bufs.expert_counts, "expert_counts", torch.int32, (E,), dev)
+    _need(bufs.expert_offsets, "expert_offsets", torch.int32, (E + 1,), dev)
+    _need(bufs.group_offsets, "group_offsets", torch.int32, (groups + 1,), dev)
+    _need(bufs.row_src, "row_src", torch.int32, (R,), dev)
+    _need(bufs.dst_row, "dst_row", torch.int32, (T, k), dev)
+    _need(bufs.workspace, "workspace", torch.uint8, None, dev)
+    _check("moe_route_dispatch", lib.moe_route_dispatch(
+        _ptr(logits), _ptr(x), T, H, E, k, groups, row_align,
+        MOE_OUT_FP8_E4M3 if fp8 else MOE_OUT_BF16, _ptr(topk_idx), _ptr(topk_w), _ptr(bufs.out),
+        _ptr(bufs.out_scales) if fp8 else None, _ptr(bufs.expert_counts),
+        _ptr(bufs.expert_offsets), _ptr(bufs.group_offsets), _ptr(bufs.row_src),
+        _ptr(bufs.dst_row), _ptr(bufs.workspace), bufs.workspace.numel(), _stream(dev)))
+    return topk_idx, topk_w, bufs
 
 
 def moe_dispatch_no_alloc(x: torch.Tensor, topk_idx: torch.Tensor, E: int, groups: int = 1,

@@ -103,9 +103,7 @@ int64_t moe_dispatch_max_rows(int64_t T, int E, int k, int row_align) {
 
 size_t moe_dispatch_workspace_bytes(int64_t T, int E, int k, int groups) {
     if (max_rows_of(T, E, k, 1) < 0 || groups < 1 || E % groups != 0) return 0;
-    size_t total = 0;
-    moe::dispatch_workspace_layout(T, E, k, &total);
-    return total;
+    return moe::dispatch_workspace(T, E, k).total;
 }
 
 }  // extern "C"
@@ -118,14 +116,17 @@ namespace {
 // nothing is launched unless every check passes. With library_ws the
 // workspace is the library's own scratch (only its size is checked); with
 // run == false the checks run and nothing is launched.
-int dispatch_impl(const void* x, const int32_t* topk_idx, int64_t T, int H, int E, int k,
-                  int groups, int row_align, int out_dtype, void* out, float* out_scales,
-                  int32_t* expert_counts, int32_t* expert_offsets, int32_t* group_offsets,
-                  int32_t* row_src, int32_t* dst_row, void* workspace, size_t workspace_bytes,
-                  hipStream_t stream, bool library_ws = false, bool run = true) {
+int dispatch_impl(const float* logits, float* topk_w, const void* x, const int32_t* topk_idx,
+                  int64_t T, int H, int E, int k, int groups, int row_align, int out_dtype,
+                  void* out, float* out_scales, int32_t* expert_counts, int32_t* expert_offsets,
+                  int32_t* group_offsets, int32_t* row_src, int32_t* dst_row, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream, bool library_ws = false,
+                  bool run = true) {
+    const bool route = logits != nullptr || topk_w != nullptr;   // moe_route_dispatch
     // sizes and options
     const int64_t max_rows = max_rows_of(T, E, k, row_align);
     if (max_rows < 0) return MOE_EINVAL;
+    if (route && T * (int64_t)E > ((int64_t)1 << 40)) return MOE_EINVAL;
     if (groups < 1 || groups > E || E % groups != 0) return MOE_EINVAL;
     if (out_dtype != MOE_OUT_BF16 && out_dtype != MOE_OUT_FP8_E4M3) return MOE_EINVAL;
     const bool fp8 = out_dtype == MOE_OUT_FP8_E4M3;
@@ -133,6 +134,8 @@ int dispatch_impl(const void* x, const int32_t* topk_idx, int64_t T, int H, int 
     moe::DispatchArgs a;
     a.x = x;
     a.topk_idx = topk_idx;
+    a.logits = logits;
+    a.topk_w = topk_w;
     a.T = T;
     a.H = H;
     a.E = E;
@@ -147,17 +150,21 @@ int dispatch_impl(const void* x, const int32_t* topk_idx, int64_t T, int H, int 
     a.group_offsets = group_offsets;
     a.row_src = row_src;
     a.dst_row = dst_row;
-    a.tile_counts = static_cast<int32_t*>(workspace);
-    size_t ws_total = 0;
-    const size_t rank_off = moe::dispatch_workspace_layout(T, E, k, &ws_total);
-    a.tile_rank = reinterpret_cast<int32_t*>(static_cast<unsigned char*>(workspace) + rank_off);
+    const moe::DispatchWorkspace ws = moe::dispatch_workspace(T, E, k);
+    unsigned char* wsb = static_cast<unsigned char*>(workspace);
+    a.ticket = reinterpret_cast<uint32_t*>(wsb);
+    a.tile_counts = reinterpret_cast<int32_t*>(wsb + ws.counts_off);
+    a.tile_rank = reinterpret_cast<int32_t*>(wsb + ws.rank_off);
     a.max_rows = max_rows;
     moe::LaunchInfo info[3];
-    (void)moe::launch_dispatch(a, nullptr, info, false);
-    if (!all_fit(info, 3)) return MOE_EINVAL;
+    int nk = 0;
+    // geometry (route_sort_applies looks only at the logits address)
+    (void)moe::launch_dispatch(a, nullptr, info, &nk, false);
+    if (!all_fit(info, nk)) return MOE_EINVAL;
     // required pointers
     if (!expert_counts || !expert_offsets) return MOE_ENULL;
     if (T > 0 && (!x || !topk_idx || !dst_row)) return MOE_ENULL;
+    if (route && T > 0 && (!logits || !topk_w)) return MOE_ENULL;
     if (max_rows > 0 && (!out || !row_src)) return MOE_ENULL;
     if (fp8 && max_rows > 0 && !out_scales) return MOE_ENULL;
     // alignment
@@ -166,17 +173,19 @@ int dispatch_impl(const void* x, const int32_t* topk_idx, int64_t T, int H, int 
         !aligned(group_offsets, 4) || !aligned(row_src, 4) || !aligned(dst_row, 4) ||
         !aligned(workspace, 4) || (fp8 && !aligned(out_scales, 4)))
         return MOE_EALIGN;
+    if (route && (!aligned(logits, 4) || !aligned(topk_w, 4))) return MOE_EALIGN;
     // workspace
-    if (workspace_bytes < ws_total) return MOE_ENOSPC;
-    if (!library_ws && ws_total > 0 && !workspace) return MOE_ENULL;
+    if (workspace_bytes < ws.total) return MOE_ENOSPC;
+    if (!library_ws && !workspace) return MOE_ENULL;
     if (!run) return MOE_OK;
 
-    const hipError_t e = moe::launch_dispatch(a, stream, info);
-    if (log_enabled()) {
-        log_launch("dispatch.tile_hist", info[0]);
-        log_launch("dispatch.scan", info[1]);
-        log_launch("dispatch.scatter", info[2]);
-    }
+    const hipError_t e = moe::launch_dispatch(a, stream, info, &nk);
+    if (log_enabled())
+        for (int i = 0; i < nk; i++)
+            log_launch(i == nk - 1 ? "dispatch.scatter"
+                       : i == nk - 2 ? (route && nk == 2 ? "dispatch.route_count" : "dispatch.count")
+                                     : "dispatch.route",
+                       info[i]);
     return status_of(e);
 }
 
@@ -189,9 +198,22 @@ int moe_dispatch(const void* x, const int32_t* topk_idx, int64_t T, int H, int E
                  int32_t* expert_counts, int32_t* expert_offsets, int32_t* group_offsets,
                  int32_t* row_src, int32_t* dst_row, void* workspace, size_t workspace_bytes,
                  void* stream) {
-    return dispatch_impl(x, topk_idx, T, H, E, k, groups, row_align, out_dtype, out, out_scales,
-                         expert_counts, expert_offsets, group_offsets, row_src, dst_row,
-                         workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+    return dispatch_impl(nullptr, nullptr, x, topk_idx, T, H, E, k, groups, row_align, out_dtype,
+                         out, out_scales, expert_counts, expert_offsets, group_offsets, row_src,
+                         dst_row, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+int moe_route_dispatch(const float* logits, const void* x, int64_t T, int H, int E, int k,
+                       int groups, int row_align, int out_dtype, int32_t* topk_idx,
+                       float* topk_w, void* out, float* out_scales, int32_t* expert_counts,
+                       int32_t* expert_offsets, int32_t* group_offsets, int32_t* row_src,
+                       int32_t* dst_row, void* workspace, size_t workspace_bytes, void* stream) {
+    // at least one of logits / topk_w must be non-null to select routing;
+    // a null one is then reported by the pointer checks
+    if (!logits && !topk_w) return T > 0 ? MOE_ENULL : MOE_OK;
+    return dispatch_impl(logits, topk_w, x, topk_idx, T, H, E, k, groups, row_align, out_dtype,
+                         out, out_scales, expert_counts, expert_offsets, group_offsets, row_src,
+                         dst_row, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"
@@ -235,17 +257,18 @@ int moe_dispatch_no_alloc(const void* x, const int32_t* topk_idx, int64_t T, int
                           void* stream) {
     // every check first, with no HIP call (a request needing more scratch
     // than the array holds fails here with MOE_ENOSPC)
-    const int st = dispatch_impl(x, topk_idx, T, H, E, k, groups, row_align, out_dtype, out,
-                                 out_scales, expert_counts, expert_offsets, group_offsets, row_src,
-                                 dst_row, nullptr, MOE_NO_ALLOC_SCRATCH_BYTES, nullptr,
-                                 /*library_ws=*/true, /*run=*/false);
+    const int st = dispatch_impl(nullptr, nullptr, x, topk_idx, T, H, E, k, groups, row_align,
+                                 out_dtype, out, out_scales, expert_counts, expert_offsets,
+                                 group_offsets, row_src, dst_row, nullptr,
+                                 MOE_NO_ALLOC_SCRATCH_BYTES, nullptr, /*library_ws=*/true,
+                                 /*run=*/false);
     if (st != MOE_OK) return st;
     void* ws = device_scratch();
     if (!ws) return MOE_EHIP;
-    return dispatch_impl(x, topk_idx, T, H, E, k, groups, row_align, out_dtype, out, out_scales,
-                         expert_counts, expert_offsets, group_offsets, row_src, dst_row, ws,
-                         MOE_NO_ALLOC_SCRATCH_BYTES, static_cast<hipStream_t>(stream),
-                         /*library_ws=*/true);
+    return dispatch_impl(nullptr, nullptr, x, topk_idx, T, H, E, k, groups, row_align, out_dtype,
+                         out, out_scales, expert_counts, expert_offsets, group_offsets, row_src,
+                         dst_row, ws, MOE_NO_ALLOC_SCRATCH_BYTES,
+                         static_cast<hipStream_t>(stream), /*library_ws=*/true);
 }
 
 int moe_combine(const void* expert_out, const int32_t* dst_row, const float* topk_w, int64_t T,

@@ -33,93 +33,95 @@
 #include "moe_device.h"
 #include "launch.h"
 
+// Dispatch: per-expert counts, segment offsets, and the stable scatter of
+// token rows into per-expert contiguous buffers (optionally FP8 with 1x128
+// scales).
+//
+// "Enabling trillion-parameter models on AWS EFA", Dispatch and Combine:
+// token counts per expert come first (accumulated with atomics in shared
+// memory), their cumulative sum gives the offsets at which tokens are packed
+// into contiguous per-expert send buffers. "Efficient and portable
+// mixture-of-experts communication", Dispatch: activations, block scales and
+// the token index are packed together; the receiver there fills its buffers
+// in a non-deterministic order, which this layout replaces with token order
+// inside every expert segment.
+//
+// Two launches on the caller's stream:
+//   count   one block per tile of TT tokens (TT = 16, 32 or 64 by T). The
+//           block ORs one bit per (token, slot) into a 64-bit mask per expert
+//           in LDS (atomic OR: a skewed expert costs no serialised counter),
+//           writes the tile's counts [tile, E] and, per slot, the token's rank
+//           within the tile for its expert (popcount of the lower tokens'
+//           bits). In moe_route_dispatch the same block first routes its
+//           tokens (top-k by sorting networks, topk_sort.h). Then it takes a
+//           ticket; the block that takes the last ticket (atomicInc wraps the
+//           counter back to zero for the next call) scans: per expert, an
+//           exclusive sum over tiles turns tile counts into each tile's first
+//           row inside the segment (this makes the order stable); totals are
+//           padded to row_align and summed over experts into offsets; group
+//           offsets are read off the expert offsets.
+//   scatter one wave per (token, row chunk): rows = tile base + in-tile rank;
+//           reads each x row once with 16-byte streaming loads and stores it
+//           to its k rows (FP8: one quantisation per token, k stores); the
+//           chunk-0 wave publishes dst_row / row_src. Leading blocks zero the
+//           pad rows.
+#include "moe_device.h"
+#include "launch.h"
+#include "topk_sort.h"
+
 namespace moe {
 
-constexpr int kHistWaves = kTileTokens / kWave;   // 4
+int dispatch_tile_tokens(int64_t T) { return T <= 1024 ? 16 : T <= 4096 ? 32 : 64; }
 
-int64_t dispatch_tiles(int64_t T) { return (T + kTileTokens - 1) / kTileTokens; }
-
-size_t dispatch_workspace_layout(int64_t T, int E, int k, size_t* total) {
-    const size_t counts = (size_t)dispatch_tiles(T) * (size_t)E * sizeof(int32_t);
-    const size_t rank_off = (counts + 255) / 256 * 256;
-    *total = rank_off + (size_t)T * (size_t)k * sizeof(int32_t);
-    return rank_off;
+int64_t dispatch_tiles(int64_t T) {
+    const int TT = dispatch_tile_tokens(T);
+    return (T + TT - 1) / TT;
 }
 
-// ---------------------------------------------------------------- K2
+DispatchWorkspace dispatch_workspace(int64_t T, int E, int k) {
+    DispatchWorkspace w;
+    w.tile_tokens = dispatch_tile_tokens(T);
+    w.tiles = dispatch_tiles(T);
+    w.counts_off = 256;   // [0, 256): the ticket counter (word 0)
+    const size_t counts = (size_t)w.tiles * (size_t)E * sizeof(int32_t);
+    w.rank_off = (w.counts_off + counts + 255) / 256 * 256;
+    w.total = w.rank_off + (size_t)T * (size_t)k * sizeof(int32_t);
+    return w;
+}
 
-__global__ __launch_bounds__(kTileTokens) void k_tile_hist(const int32_t* __restrict__ topk_idx,
-                                                           int64_t T, int E, int k,
-                                                           int32_t* __restrict__ tile_counts,
-                                                           int32_t* __restrict__ tile_rank) {
-    extern __shared__ __align__(16) unsigned char smem[];
-    uint64_t* mask = reinterpret_cast<uint64_t*>(smem);               // [waves][E]
-    int32_t* before = reinterpret_cast<int32_t*>(mask + kHistWaves * E);  // [waves][E]
+static int pow2_at_least(int n) {
+    int p = 1;
+    while (p < n) p <<= 1;
+    return p;
+}
 
+// ---------------------------------------------------------------- count
+
+// Tile histogram and in-tile ranks. ids(p) is the expert of pair p = tl * k + j
+// of the tile (token tl, slot j), npairs = tokens in the tile * k. Writes the
+// tile's counts tile_counts[tile * E + e] and rank[p] (the tile's slice of the
+// [T, k] rank array; -1 for a slot whose expert is outside [0, E)).
+template <typename Ids>
+__device__ __forceinline__ void count_tile(Ids ids, int npairs, int k, int E, int64_t tile,
+                                           uint64_t* s_mask, int32_t* __restrict__ tile_counts,
+                                           int32_t* __restrict__ rank) {
+    const int NT = blockDim.x;
     const int tid = threadIdx.x;
-    const int w = tid / kWave;
-    const int lane = tid & (kWave - 1);
-    const int64_t t = (int64_t)blockIdx.x * kTileTokens + tid;
-    const bool live = t < T;
-
-    for (int i = tid; i < kHistWaves * E; i += kTileTokens) mask[i] = 0ull;
+    for (int i = tid; i < E; i += NT) s_mask[i] = 0ull;
     __syncthreads();
-
-    // expert ids are loaded in batches of 8 before any LDS atomic, so the
-    // loads are in flight together; the first batch stays in registers for
-    // the ranking pass
-    const uint64_t bit = 1ull << lane;
-    int e0[8];
-#pragma unroll
-    for (int jj = 0; jj < 8; jj++) e0[jj] = (live && jj < k) ? topk_idx[t * k + jj] : -1;
-#pragma unroll
-    for (int jj = 0; jj < 8; jj++)
-        if ((unsigned)e0[jj] < (unsigned)E) atomicOr(&mask[w * E + e0[jj]], bit);
-    if (live) {
-        for (int j0 = 8; j0 < k; j0 += 8) {
-            int e[8];
-#pragma unroll
-            for (int jj = 0; jj < 8; jj++) e[jj] = (j0 + jj < k) ? topk_idx[t * k + j0 + jj] : -1;
-#pragma unroll
-            for (int jj = 0; jj < 8; jj++)
-                if ((unsigned)e[jj] < (unsigned)E) atomicOr(&mask[w * E + e[jj]], bit);
-        }
+    for (int p = tid; p < npairs; p += NT) {
+        const int e = ids(p);
+        if ((unsigned)e < (unsigned)E) atomicOr(&s_mask[e], 1ull << (p / k));
     }
     __syncthreads();
-
-    for (int e = tid; e < E; e += kTileTokens) {
-        int run = 0;
-#pragma unroll
-        for (int v = 0; v < kHistWaves; v++) {
-            before[v * E + e] = run;
-            run += __popcll(mask[v * E + e]);
-        }
-        tile_counts[(int64_t)blockIdx.x * E + e] = run;
-    }
-    __syncthreads();
-
-    if (live) {
-        const uint64_t lower = bit - 1ull;
-        for (int j0 = 0; j0 < k; j0 += 8) {
-            int e[8];
-#pragma unroll
-            for (int jj = 0; jj < 8; jj++)
-                e[jj] = j0 == 0 ? e0[jj] : ((j0 + jj < k) ? topk_idx[t * k + j0 + jj] : -1);
-#pragma unroll
-            for (int jj = 0; jj < 8; jj++) {
-                if (j0 + jj >= k) break;
-                int r = -1;
-                if ((unsigned)e[jj] < (unsigned)E)
-                    r = before[w * E + e[jj]] + __popcll(mask[w * E + e[jj]] & lower);
-                tile_rank[t * k + j0 + jj] = r;
-            }
-        }
+    for (int i = tid; i < E; i += NT) tile_counts[tile * E + i] = __popcll(s_mask[i]);
+    for (int p = tid; p < npairs; p += NT) {
+        const int e = ids(p);
+        int r = -1;
+        if ((unsigned)e < (unsigned)E) r = __popcll(s_mask[e] & ((1ull << (p / k)) - 1ull));
+        rank[p] = r;
     }
 }
-
-// ---------------------------------------------------------------- K3
-
-constexpr int kScanThreads = 1024;
 
 __device__ __forceinline__ int wave_inclusive_sum(int v) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -131,28 +133,45 @@ __device__ __forceinline__ int wave_inclusive_sum(int v) {
     return v;
 }
 
-// Threads are laid out as tid = p * Ep + e (Ep = E rounded up to a power of
-// two): P = 1024 / Ep threads share expert e, thread p owning a contiguous
-// range of tiles. Pass 1 sums each range with independent loads in batches of
-// 8; an LDS exchange gives each range its start inside the expert's segment;
-// the p == 0 threads scan the padded totals over experts; pass 2 rewrites the
-// tile counts as tile bases (segment offset + rows of earlier tiles).
-__global__ __launch_bounds__(kScanThreads) void k_scan(int32_t* __restrict__ tile_counts,
-                                                       int64_t tiles, int E, int row_align,
-                                                       int groups,
-                                                       int32_t* __restrict__ expert_counts,
-                                                       int32_t* __restrict__ expert_offsets,
-                                                       int32_t* __restrict__ group_offsets) {
-    __shared__ int32_t s_part[kScanThreads];
-    __shared__ int32_t s_off[1025];
-    __shared__ int32_t s_wave[kScanThreads / kWave];
+// True in every thread of the block that finishes last. Each block's global
+// writes are released (device-scope fence) before it takes its ticket; the
+// last block acquires before it reads what the others wrote. atomicInc wraps
+// the counter to zero on the last ticket, ready for the next launch.
+__device__ __forceinline__ bool last_block(uint32_t* ticket) {
+    __shared__ int s_last;
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) s_last = atomicInc(ticket, gridDim.x - 1) == gridDim.x - 1;
+    __syncthreads();
+    const bool last = s_last != 0;
+    if (last) __threadfence();
+    return last;
+}
 
+constexpr int kScanBatch = 16;
+
+// Scan over tiles by one block of NT >= Ep threads (Ep = E rounded up to a
+// power of two), laid out as tid = p * Ep + e: P = NT / Ep threads share
+// expert e, thread p owning a contiguous range of tiles. Pass 1 sums each
+// range with batches of independent loads; an LDS exchange gives each range
+// its start inside the expert's segment; the p == 0 threads (tid 0 .. Ep-1,
+// in expert order) scan the padded totals over experts; pass 2 rewrites the
+// tile counts as tile bases (segment offset + rows of earlier tiles).
+__device__ void scan_tiles(int32_t* __restrict__ tile_counts, int64_t tiles, int E, int row_align,
+                           int groups, int32_t* __restrict__ expert_counts,
+                           int32_t* __restrict__ expert_offsets,
+                           int32_t* __restrict__ group_offsets) {
+    __shared__ int32_t s_part[1024];
+    __shared__ int32_t s_off[kMaxExperts + 1];
+    __shared__ int32_t s_wave[1024 / kWave];
+
+    const int NT = blockDim.x;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
     int Ep = 1;
     while (Ep < E) Ep <<= 1;
-    const int P = kScanThreads / Ep;
+    const int P = NT / Ep;
     const int e = tid & (Ep - 1);
     const int p = tid / Ep;
     const bool real = e < E;
@@ -160,21 +179,15 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(int32_t* __restrict__ til
     const int64_t b0 = min(tiles, (int64_t)p * per);
     const int64_t b1 = min(tiles, b0 + per);
 
-    // pass 1: rows of this expert in tiles [b0, b1); the first 8 counts stay
-    // in registers for pass 2
     int part = 0;
-    int c0[8];
-#pragma unroll
-    for (int i = 0; i < 8; i++) c0[i] = (real && b0 + i < b1) ? tile_counts[(b0 + i) * E + e] : 0;
-#pragma unroll
-    for (int i = 0; i < 8; i++) part += c0[i];
     if (real) {
-        for (int64_t b = b0 + 8; b < b1; b += 8) {
-            int c[8];
+        for (int64_t b = b0; b < b1; b += kScanBatch) {
+            int c[kScanBatch];
 #pragma unroll
-            for (int i = 0; i < 8; i++) c[i] = (b + i < b1) ? tile_counts[(b + i) * E + e] : 0;
+            for (int i = 0; i < kScanBatch; i++)
+                c[i] = (b + i < b1) ? tile_counts[(b + i) * E + e] : 0;
 #pragma unroll
-            for (int i = 0; i < 8; i++) part += c[i];
+            for (int i = 0; i < kScanBatch; i++) part += c[i];
         }
     }
     s_part[tid] = part;
@@ -187,15 +200,15 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(int32_t* __restrict__ til
     }
     const int padded = (p == 0 && real) ? (cnt + row_align - 1) / row_align * row_align : 0;
 
-    // exclusive scan of the padded totals over experts (the p == 0 threads
-    // are tid 0 .. Ep-1, in expert order; all others add zero)
+    // exclusive scan of the padded totals over experts (only the p == 0
+    // threads contribute; they come first, in expert order)
     const int incl = wave_inclusive_sum(padded);
     if (lane == kWave - 1) s_wave[wave] = incl;
     __syncthreads();
     if (wave == 0) {
-        const int v = lane < kScanThreads / kWave ? s_wave[lane] : 0;
+        const int v = lane < NT / kWave ? s_wave[lane] : 0;
         const int vi = wave_inclusive_sum(v);
-        if (lane < kScanThreads / kWave) s_wave[lane] = vi - v;   // exclusive over waves
+        if (lane < NT / kWave) s_wave[lane] = vi - v;
     }
     __syncthreads();
     const int excl = s_wave[wave] + incl - padded;
@@ -210,18 +223,17 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(int32_t* __restrict__ til
     }
     __syncthreads();
     if (group_offsets != nullptr)
-        for (int g = tid; g <= groups; g += kScanThreads) group_offsets[g] = s_off[g * (E / groups)];
+        for (int gi = tid; gi <= groups; gi += NT) group_offsets[gi] = s_off[gi * (E / groups)];
 
-    // pass 2: tile bases
     if (real) {
         int run = s_off[e] + before;
-        for (int64_t b = b0; b < b1; b += 8) {
-            int c[8];
+        for (int64_t b = b0; b < b1; b += kScanBatch) {
+            int c[kScanBatch];
 #pragma unroll
-            for (int i = 0; i < 8; i++)
-                c[i] = b == b0 ? c0[i] : ((b + i < b1) ? tile_counts[(b + i) * E + e] : 0);
+            for (int i = 0; i < kScanBatch; i++)
+                c[i] = (b + i < b1) ? tile_counts[(b + i) * E + e] : 0;
 #pragma unroll
-            for (int i = 0; i < 8; i++)
+            for (int i = 0; i < kScanBatch; i++)
                 if (b + i < b1) {
                     tile_counts[(b + i) * E + e] = run;
                     run += c[i];
@@ -230,24 +242,87 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(int32_t* __restrict__ til
     }
 }
 
+struct CountArgs {
+    int64_t T;
+    int E, k, TT, row_align, groups;
+    int64_t tiles;
+    uint32_t* ticket;
+    int32_t* tile_counts;
+    int32_t* tile_rank;
+    int32_t* expert_counts;
+    int32_t* expert_offsets;
+    int32_t* group_offsets;
+};
+
+// Count + scan from a given routing table [T, k]. One block per tile (at
+// least one block, which then only scans: T == 0 writes zero counts).
+__global__ __launch_bounds__(1024) void k_count(const int32_t* __restrict__ topk_idx,
+                                                CountArgs a) {
+    extern __shared__ uint64_t s_mask[];   // [E]
+    const int64_t tile = blockIdx.x;
+    if (tile < a.tiles) {
+        const int64_t t0 = tile * a.TT;
+        const int n = (int)min((int64_t)a.TT, a.T - t0);
+        const int32_t* ids = topk_idx + t0 * a.k;
+        count_tile([ids](int p) { return ids[p]; }, n * a.k, a.k, a.E, tile, s_mask,
+                   a.tile_counts, a.tile_rank + t0 * a.k);
+    }
+    if (last_block(a.ticket))
+        scan_tiles(a.tile_counts, a.tiles, a.E, a.row_align, a.groups, a.expert_counts,
+                   a.expert_offsets, a.group_offsets);
+}
+
+// Route + count + scan: the tile's TT tokens are routed first by TT * S
+// threads (S lanes per token), their experts kept in LDS for the count.
+template <int S, int K>
+__global__ __launch_bounds__(1024) void k_route_count(const float* __restrict__ logits,
+                                                      int32_t* __restrict__ topk_idx,
+                                                      float* __restrict__ topk_w, CountArgs a) {
+    extern __shared__ uint64_t s_mask[];   // [E], then the tile's experts [TT * k]
+    int32_t* s_ids = reinterpret_cast<int32_t*>(s_mask + a.E);
+    const int64_t tile = blockIdx.x;
+    if (tile < a.tiles) {
+        const int64_t t0 = tile * a.TT;
+        const int n = (int)min((int64_t)a.TT, a.T - t0);
+        if ((int)threadIdx.x < a.TT * S) {   // whole lane groups
+            const int tl = threadIdx.x / S;
+            const int g = threadIdx.x & (S - 1);
+            const int64_t t = t0 + tl;
+            const bool live = tl < n;
+            double list[K];
+            route_token<S, K>(logits + (live ? t : 0) * (int64_t)a.E, live, a.E, g, list);
+            if (live)
+                write_route<S, K>(list, g, t, tl, a.E, a.k, a.k, 0, 0.0f, topk_idx, topk_w, s_ids);
+        }
+        __syncthreads();
+        count_tile([s_ids](int p) { return s_ids[p]; }, n * a.k, a.k, a.E, tile, s_mask,
+                   a.tile_counts, a.tile_rank + t0 * a.k);
+    }
+    if (last_block(a.ticket))
+        scan_tiles(a.tile_counts, a.tiles, a.E, a.row_align, a.groups, a.expert_counts,
+                   a.expert_offsets, a.group_offsets);
+}
+
 // ---------------------------------------------------------------- K4
 
 constexpr int kScatterThreads = 256;
 
 // Zero the pad rows of one expert's segment, or the part of them this
 // block owns (pad rows of expert e: [offsets[e] + counts[e], offsets[e+1])).
+// Rows outside [0, max_rows) are never written, whatever the offsets say.
 __device__ void zero_pad_rows(int pb, int pad_blocks_per_expert, int pad_rows_per_block, int H,
-                              bool fp8, const int32_t* __restrict__ expert_counts,
+                              bool fp8, int64_t max_rows,
+                              const int32_t* __restrict__ expert_counts,
                               const int32_t* __restrict__ expert_offsets,
                               unsigned char* __restrict__ out, float* __restrict__ scales,
                               int32_t* __restrict__ row_src) {
     const int e = pb / pad_blocks_per_expert;
     const int part = pb - e * pad_blocks_per_expert;
-    const int first = expert_offsets[e] + expert_counts[e];
-    const int npad = expert_offsets[e + 1] - first;
+    const int64_t first = (int64_t)expert_offsets[e] + expert_counts[e];
+    const int64_t npad = min((int64_t)expert_offsets[e + 1], max_rows) - first;
     const int lo = part * pad_rows_per_block;
-    const int hi = min(npad, lo + pad_rows_per_block);
-    if (lo >= hi) return;
+    const int hi = (int)min(npad, (int64_t)lo + pad_rows_per_block);
+    if (first < 0 || lo >= hi) return;
     const int rows = hi - lo;
     const int64_t row_bytes = fp8 ? (int64_t)H : 2 * (int64_t)H;
     const int units = (int)(row_bytes / 16);
@@ -308,11 +383,11 @@ __global__ __launch_bounds__(kScatterThreads) void k_scatter_bf16(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ topk_idx,
     const int32_t* __restrict__ tile_rank, const int32_t* __restrict__ tile_base,
     const int32_t* __restrict__ expert_counts, const int32_t* __restrict__ expert_offsets,
-    int64_t T, int H, int E, int k, int64_t max_rows, int pad_blocks,
+    int64_t T, int H, int E, int k, int TT, int64_t max_rows, int pad_blocks,
     int pad_blocks_per_expert, int pad_rows_per_block, unsigned char* __restrict__ out,
     int32_t* __restrict__ row_src, int32_t* __restrict__ dst_row) {
     if ((int)blockIdx.x < pad_blocks) {
-        zero_pad_rows(blockIdx.x, pad_blocks_per_expert, pad_rows_per_block, H, false,
+        zero_pad_rows(blockIdx.x, pad_blocks_per_expert, pad_rows_per_block, H, false, max_rows,
                       expert_counts, expert_offsets, out, nullptr, row_src);
         return;
     }
@@ -328,7 +403,7 @@ __global__ __launch_bounds__(kScatterThreads) void k_scatter_bf16(
 
     const uint4 a = load16_nt(range_rsrc(x + t * (int64_t)H, 2 * H), 16 * u);
     const int64_t p0 = t * k;
-    const int32_t* tb = tile_base + (t / kTileTokens) * E;
+    const int32_t* tb = tile_base + (t / TT) * E;
     for (int j0 = 0; j0 < k; j0 += 8) {
         int r[8];
         slot_rows(topk_idx, tile_rank, tb, p0, j0, k, E, max_rows, r);
@@ -353,12 +428,12 @@ __global__ __launch_bounds__(1024) void k_scatter_fp8(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ topk_idx,
     const int32_t* __restrict__ tile_rank, const int32_t* __restrict__ tile_base,
     const int32_t* __restrict__ expert_counts, const int32_t* __restrict__ expert_offsets,
-    int64_t T, int H, int E, int k, int64_t max_rows, int pad_blocks,
+    int64_t T, int H, int E, int k, int TT, int64_t max_rows, int pad_blocks,
     int pad_blocks_per_expert, int pad_rows_per_block, unsigned char* __restrict__ out,
     float* __restrict__ scales, int32_t* __restrict__ row_src, int32_t* __restrict__ dst_row) {
     extern __shared__ float s_scale[];             // [H / 128]
     if ((int)blockIdx.x < pad_blocks) {
-        zero_pad_rows(blockIdx.x, pad_blocks_per_expert, pad_rows_per_block, H, true,
+        zero_pad_rows(blockIdx.x, pad_blocks_per_expert, pad_rows_per_block, H, true, max_rows,
                       expert_counts, expert_offsets, out, scales, row_src);
         return;
     }
@@ -371,7 +446,7 @@ __global__ __launch_bounds__(1024) void k_scatter_fp8(
     const int nb = H / 128;
     const auto xr = range_rsrc(x + t * (int64_t)H, 2 * H);
     const int64_t p0 = t * k;
-    const int32_t* tb = tile_base + (t / kTileTokens) * E;
+    const int32_t* tb = tile_base + (t / TT) * E;
 
     for (int chunk = w; chunk < CW; chunk += W) {
         const int u = chunk * kWave + lane;
@@ -418,13 +493,42 @@ __global__ __launch_bounds__(1024) void k_scatter_fp8(
 
 // ---------------------------------------------------------------- launch
 
-hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream, LaunchInfo info[3],
-                           bool run) {
-    const int64_t tiles = dispatch_tiles(a.T);
-    hipError_t err;
+template <int S, int K>
+static void launch_route_count_sk(const DispatchArgs& a, const CountArgs& c, int64_t grid,
+                                  int threads, size_t lds, hipStream_t stream) {
+    k_route_count<S, K><<<dim3((unsigned)grid), dim3(threads), lds, stream>>>(
+        a.logits, const_cast<int32_t*>(a.topk_idx), a.topk_w, c);
+}
 
-    // geometry of the three kernels first
-    const size_t hist_lds = (size_t)kHistWaves * a.E * (sizeof(uint64_t) + sizeof(int32_t));
+template <int K>
+static void launch_route_count_k(int S, const DispatchArgs& a, const CountArgs& c, int64_t grid,
+                                 int threads, size_t lds, hipStream_t stream) {
+    switch (S) {
+        case 1: launch_route_count_sk<1, K>(a, c, grid, threads, lds, stream); break;
+        case 2: launch_route_count_sk<2, K>(a, c, grid, threads, lds, stream); break;
+        case 4: launch_route_count_sk<4, K>(a, c, grid, threads, lds, stream); break;
+        case 8: launch_route_count_sk<8, K>(a, c, grid, threads, lds, stream); break;
+        default: launch_route_count_sk<16, K>(a, c, grid, threads, lds, stream); break;
+    }
+}
+
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream, LaunchInfo info[3], int* n,
+                           bool run) {
+    const DispatchWorkspace ws = dispatch_workspace(a.T, a.E, a.k);
+    const int TT = ws.tile_tokens;
+    const int64_t tiles = ws.tiles;
+    const int Ep = pow2_at_least(a.E);
+    // routing inside the count kernel when the sorting-network path applies
+    const bool fused = a.logits != nullptr && route_sort_applies(a.logits, a.E, a.k);
+    const bool route_first = a.logits != nullptr && !fused;
+    const int S = fused ? route_lanes(a.E) : 1;
+    int count_threads = fused ? TT * S : 256;
+    if (count_threads < Ep) count_threads = Ep;
+    if (count_threads < kWave) count_threads = kWave;
+    const size_t count_lds = (size_t)a.E * sizeof(uint64_t) +
+                             (fused ? (size_t)TT * a.k * sizeof(int32_t) : 0);
+    const int64_t count_grid = tiles > 0 ? tiles : 1;
+
     int pad_per_expert = 0, pad_rows_per_block = 0;
     if (a.row_align > 1 && a.T > 0) {
         pad_per_expert = a.row_align - 1 < 4 ? a.row_align - 1 : 4;
@@ -438,44 +542,59 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream, LaunchInfo
     const int64_t scatter_blocks =
         a.fp8 ? pad_blocks + a.T
               : pad_blocks + (a.T * bf16_waves_per_token + kScatterWaves - 1) / kScatterWaves;
+
+    int nk = 0;
+    LaunchInfo route_info;
+    if (route_first)
+        (void)launch_route_topk(a.logits, a.T, a.E, a.k, 0, 0.0f, const_cast<int32_t*>(a.topk_idx),
+                                a.topk_w, stream, &route_info, false);
     if (info) {
-        info[0] = LaunchInfo{tiles, kTileTokens, hist_lds, 0};
-        info[1] = LaunchInfo{1, kScanThreads, 0, 0};
-        info[2] = a.fp8 ? LaunchInfo{scatter_blocks, fp8_threads,
-                                     (size_t)(a.H / 128) * sizeof(float), fp8_waves}
-                        : LaunchInfo{scatter_blocks, kScatterThreads, 0, bf16_waves_per_token};
+        if (route_first) info[nk++] = route_info;
+        info[nk++] = LaunchInfo{count_grid, count_threads, count_lds, fused ? S : TT};
+        info[nk++] = a.fp8 ? LaunchInfo{scatter_blocks, fp8_threads,
+                                        (size_t)(a.H / 128) * sizeof(float), fp8_waves}
+                           : LaunchInfo{scatter_blocks, kScatterThreads, 0, bf16_waves_per_token};
+    } else {
+        nk = route_first ? 3 : 2;
     }
+    if (n) *n = nk;
     if (!run) return hipSuccess;
 
-    // K2
-    if (tiles > 0) {
-        k_tile_hist<<<dim3((unsigned)tiles), dim3(kTileTokens), hist_lds, stream>>>(
-            a.topk_idx, a.T, a.E, a.k, a.tile_counts, a.tile_rank);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipError_t err;
+    if (route_first) {
+        err = launch_route_topk(a.logits, a.T, a.E, a.k, 0, 0.0f, const_cast<int32_t*>(a.topk_idx),
+                                a.topk_w, stream, nullptr);
+        if (err != hipSuccess) return err;
     }
-
-    // K3
-    k_scan<<<1, kScanThreads, 0, stream>>>(a.tile_counts, tiles, a.E, a.row_align, a.groups,
-                                            a.expert_counts, a.expert_offsets, a.group_offsets);
+    const CountArgs c{a.T, a.E, a.k, TT, a.row_align, a.groups, tiles, a.ticket, a.tile_counts,
+                      a.tile_rank, a.expert_counts, a.expert_offsets, a.group_offsets};
+    if (fused) {
+        switch (route_list_len(a.k)) {
+            case 2: launch_route_count_k<2>(S, a, c, count_grid, count_threads, count_lds, stream); break;
+            case 4: launch_route_count_k<4>(S, a, c, count_grid, count_threads, count_lds, stream); break;
+            default: launch_route_count_k<8>(S, a, c, count_grid, count_threads, count_lds, stream); break;
+        }
+    } else {
+        k_count<<<dim3((unsigned)count_grid), dim3(count_threads), count_lds, stream>>>(a.topk_idx,
+                                                                                        c);
+    }
     if ((err = hipGetLastError()) != hipSuccess) return err;
 
-    // K4: leading blocks zero pad rows, then the token work
+    // scatter: leading blocks zero pad rows, then the token work
     unsigned char* out = static_cast<unsigned char*>(a.out);
     const uint16_t* x = static_cast<const uint16_t*>(a.x);
+    if (scatter_blocks == 0) return hipSuccess;
     if (a.fp8) {
-        // one block per token, one wave per 64-unit chunk (at most 16 waves)
         const size_t lds = (size_t)(a.H / 128) * sizeof(float);
-        if (scatter_blocks == 0) return hipSuccess;
         k_scatter_fp8<<<dim3((unsigned)scatter_blocks), dim3(fp8_threads), lds, stream>>>(
             x, a.topk_idx, a.tile_rank, a.tile_counts, a.expert_counts, a.expert_offsets, a.T,
-            a.H, a.E, a.k, a.max_rows, (int)pad_blocks, pad_per_expert, pad_rows_per_block, out,
-            a.out_scales, a.row_src, a.dst_row);
+            a.H, a.E, a.k, TT, a.max_rows, (int)pad_blocks, pad_per_expert, pad_rows_per_block,
+            out, a.out_scales, a.row_src, a.dst_row);
     } else {
-        if (scatter_blocks == 0) return hipSuccess;
         k_scatter_bf16<<<dim3((unsigned)scatter_blocks), dim3(kScatterThreads), 0, stream>>>(
             x, a.topk_idx, a.tile_rank, a.tile_counts, a.expert_counts, a.expert_offsets, a.T,
-            a.H, a.E, a.k, a.max_rows, (int)pad_blocks, pad_per_expert, pad_rows_per_block, out,
-            a.row_src, a.dst_row);
+            a.H, a.E, a.k, TT, a.max_rows, (int)pad_blocks, pad_per_expert, pad_rows_per_block,
+            out, a.row_src, a.dst_row);
     }
     return hipGetLastError();
 }

@@ -8,8 +8,8 @@
 
 namespace moe {
 
-// Tokens per tile of the dispatch histogram (one thread per token).
-constexpr int kTileTokens = 256;
+// Largest expert count the kernels accept (MOE_MAX_EXPERTS of the C ABI).
+constexpr int kMaxExperts = 1024;
 
 struct LaunchInfo {
     int64_t grid = 0;
@@ -38,7 +38,9 @@ hipError_t launch_route_replicas(int32_t* topk_idx, int64_t T, int k, int E,
 
 struct DispatchArgs {
     const void* x;
-    const int32_t* topk_idx;
+    const int32_t* topk_idx;     // routing table; written here first when logits != nullptr
+    const float* logits;         // [T, E]: route inside the dispatch (moe_route_dispatch), or nullptr
+    float* topk_w;               // [T, k] router weights out, with logits
     int64_t T;
     int H, E, k, groups, row_align;
     bool fp8;
@@ -49,18 +51,29 @@ struct DispatchArgs {
     int32_t* group_offsets;
     int32_t* row_src;
     int32_t* dst_row;
+    uint32_t* ticket;       // workspace word 0: zero before the first call, zero after each
     int32_t* tile_counts;   // workspace [tiles, E]
     int32_t* tile_rank;     // workspace [T, k]
     int64_t max_rows;       // rows in out / out_scales / row_src
 };
 
+// Tokens per count tile (16, 32 or 64, growing with T) and the tile count.
+int dispatch_tile_tokens(int64_t T);
 int64_t dispatch_tiles(int64_t T);
 
-// Workspace layout: tile counts [tiles, E], then (256-byte aligned) in-tile
-// ranks [T, k]. Returns the byte offset of the ranks; *total gets the size.
-size_t dispatch_workspace_layout(int64_t T, int E, int k, size_t* total);
+// Workspace layout: [0, 256) control (the ticket counter in word 0), tile
+// counts [tiles, E] at counts_off, then (256-byte aligned) in-tile ranks
+// [T, k] at rank_off; total bytes.
+struct DispatchWorkspace {
+    int tile_tokens;
+    int64_t tiles;
+    size_t counts_off, rank_off, total;
+};
+DispatchWorkspace dispatch_workspace(int64_t T, int E, int k);
 
-hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream, LaunchInfo info[3],
+// Up to three kernels: [route (only when routing falls back to its own
+// kernel)], count + scan, scatter. *n gets the number of kernels.
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream, LaunchInfo info[3], int* n,
                            bool run = true);
 
 hipError_t launch_combine(const void* expert_out, const int32_t* dst_row, const float* topk_w,

@@ -1,6 +1,11 @@
 // K1: router gate. Per token: top-k experts by logit and their softmax
 // weights renormalised over the chosen k.
 //
+// Two kernels. k_route_sort (k <= 8, E <= 768, E % 4 == 0, 16-byte aligned
+// rows) sorts packed candidates with compare-exchange networks (topk_sort.h).
+// k_route_topk below handles every other shape (k up to 1024, any E) in k
+// rounds of a wave-wide maximum.
+//
 // "Efficient and portable mixture-of-experts communication", Introduction:
 // the router is a small linear layer giving a probability distribution over
 // experts; the top-K experts are used and the output is their weighted
@@ -23,6 +28,7 @@
 // k > 64), which then writes slot r of the output.
 #include "moe_device.h"
 #include "launch.h"
+#include "topk_sort.h"
 
 namespace moe {
 
@@ -215,6 +221,22 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_topk(const float* __res
     }
 }
 
+// Sorting-network path: S lanes per token, 256 / S tokens per block.
+template <int S, int K>
+__global__ __launch_bounds__(kRouteThreads) void k_route_sort(
+    const float* __restrict__ logits, int64_t T, int E, int k, int ks, int n_shared,
+    float shared_w, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+    const int tl = threadIdx.x / S;
+    const int g = threadIdx.x & (S - 1);
+    const int64_t t = (int64_t)blockIdx.x * (kRouteThreads / S) + tl;
+    const bool live = t < T;
+    double list[K];
+    route_token<S, K>(logits + (live ? t : 0) * (int64_t)E, live, E, g, list);
+    if (live)
+        write_route<S, K>(list, g, t, tl, E, k, ks, n_shared, shared_w, topk_idx, topk_w,
+                          nullptr);
+}
+
 struct RouteArgs {
     const float* logits;
     int64_t T;
@@ -230,9 +252,40 @@ static void launch_s(const RouteArgs& a, hipStream_t stream, int64_t blocks) {
         a.logits, a.T, a.E, a.k, a.ks, a.n_shared, a.shared_w, a.topk_idx, a.topk_w);
 }
 
+template <int S, int K>
+static void launch_sort(const RouteArgs& a, hipStream_t stream, int64_t blocks) {
+    k_route_sort<S, K><<<dim3((unsigned)blocks), dim3(kRouteThreads), 0, stream>>>(
+        a.logits, a.T, a.E, a.k, a.ks, a.n_shared, a.shared_w, a.topk_idx, a.topk_w);
+}
+
+template <int K>
+static void launch_sort_k(int S, const RouteArgs& a, hipStream_t stream, int64_t blocks) {
+    switch (S) {
+        case 1: launch_sort<1, K>(a, stream, blocks); break;
+        case 2: launch_sort<2, K>(a, stream, blocks); break;
+        case 4: launch_sort<4, K>(a, stream, blocks); break;
+        case 8: launch_sort<8, K>(a, stream, blocks); break;
+        default: launch_sort<16, K>(a, stream, blocks); break;
+    }
+}
+
 hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k, int n_shared,
                              float shared_w, int32_t* topk_idx, float* topk_w,
                              hipStream_t stream, LaunchInfo* info, bool run) {
+    if (route_sort_applies(logits, E, k)) {
+        const int S = route_lanes(E);
+        const int64_t tokens_per_block = kRouteThreads / S;
+        const int64_t blocks = (T + tokens_per_block - 1) / tokens_per_block;
+        if (info) *info = LaunchInfo{blocks, kRouteThreads, 0, S};
+        if (!run || blocks == 0) return hipSuccess;
+        const RouteArgs a{logits, T, E, k, k + n_shared, n_shared, shared_w, topk_idx, topk_w};
+        switch (route_list_len(k)) {
+            case 2: launch_sort_k<2>(S, a, stream, blocks); break;
+            case 4: launch_sort_k<4>(S, a, stream, blocks); break;
+            default: launch_sort_k<8>(S, a, stream, blocks); break;
+        }
+        return hipGetLastError();
+    }
     int S = 1;
     while (S < E && S < kWave) S <<= 1;
     const int nv = (E + S - 1) / S;

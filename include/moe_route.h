@@ -4,9 +4,9 @@
  * A plain C ABI over hand-written HIP kernels. Every pointer argument named
  * "device" is device memory owned by the caller; the library allocates
  * nothing, keeps no global mutable state and only enqueues work on `stream`
- * (a hipStream_t; NULL means the default stream). Nothing is copied back to
- * the host: the number of rows dispatch produced stays on the device
- * (expert_offsets[E]) and buffers are sized by capacity.
+ * (a hipStream_t passed as void*; NULL means the default stream). Nothing is
+ * copied back to the host: the number of rows dispatch produced stays on the
+ * device (expert_offsets[E]) and buffers are sized by capacity.
  *
  * The path, after the Perplexity posts "Efficient and portable
  * mixture-of-experts communication" (sections Introduction, Dispatch,
@@ -17,6 +17,7 @@
  *   logits --moe_route_topk--> topk_idx, topk_w
  *   x, topk_idx --moe_dispatch--> per-expert contiguous rows (+ FP8 scales),
  *                                 counts, offsets, group offsets, row maps
+ *   (or both in one call: logits, x --moe_route_dispatch--> all of the above)
  *   (experts run on the rows)
  *   expert rows, dst_row, topk_w --moe_combine--> y
  *
@@ -108,8 +109,12 @@ int moe_route_replicas(int32_t* topk_idx, int64_t T, int k, int E,
  * invalid or the count does not fit in int32. */
 int64_t moe_dispatch_max_rows(int64_t T, int E, int k, int row_align);
 
-/* Workspace bytes moe_dispatch needs (per-tile expert counts); 0 on invalid
- * arguments. The workspace holds no state between calls. */
+/* Workspace bytes moe_dispatch and moe_route_dispatch need (a control word,
+ * per-tile expert counts and in-tile ranks); 0 on invalid arguments.
+ * The workspace must be zero-filled before its first use (e.g. once, right
+ * after allocation); every completed call leaves its control word at zero
+ * again, so a workspace can then be reused without clearing. The rest holds
+ * nothing between calls. Calls sharing a workspace must not overlap. */
 size_t moe_dispatch_workspace_bytes(int64_t T, int E, int k, int groups);
 
 /*
@@ -153,10 +158,12 @@ size_t moe_dispatch_workspace_bytes(int64_t T, int E, int k, int groups);
  *   row_src        device int32 [max_rows] out: t*k+j of the pair in each
  *                  row, -1 for pad rows
  *   dst_row        device int32 [T, k] out: the row holding each pair
- *   workspace      device, >= moe_dispatch_workspace_bytes, 4-byte aligned
+ *   workspace      device, >= moe_dispatch_workspace_bytes, 4-byte aligned,
+ *                  zero-filled before its first use (see above)
  * Rows at and beyond expert_offsets[E] are left untouched. max_rows is
  * moe_dispatch_max_rows(T, E, k, row_align). T == 0 writes zero counts and
- * offsets.
+ * offsets. Two kernels: counts, offsets and ranks in one launch, the rows in
+ * a second.
  */
 int moe_dispatch(const void* x, const int32_t* topk_idx,
                  int64_t T, int H, int E, int k, int groups, int row_align,
@@ -164,6 +171,31 @@ int moe_dispatch(const void* x, const int32_t* topk_idx,
                  int32_t* expert_counts, int32_t* expert_offsets,
                  int32_t* group_offsets, int32_t* row_src, int32_t* dst_row,
                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_route_topk followed by moe_dispatch in one call, with the same results
+ * as the two calls: the router's top-k and weights ("Efficient and portable
+ * mixture-of-experts communication", Introduction) feed the counts, offsets
+ * and packing of "Enabling trillion-parameter models on AWS EFA", Dispatch
+ * and Combine. When k <= 8, E <= 768, E % 4 == 0 and logits is 16-byte
+ * aligned, routing runs inside the counting kernel (two launches in all);
+ * otherwise moe_route_topk's kernel runs first (three launches).
+ *
+ *   logits         device fp32 [T, E], finite, 4-byte aligned
+ *   topk_idx       device int32 [T, k] out (as moe_route_topk), then read by
+ *                  the packing
+ *   topk_w         device fp32 [T, k] out (as moe_route_topk)
+ *   other arguments, limits and outputs as for moe_dispatch; the workspace
+ *   (moe_dispatch_workspace_bytes) follows the same zero-before-first-use
+ *   rule.
+ */
+int moe_route_dispatch(const float* logits, const void* x,
+                       int64_t T, int H, int E, int k, int groups, int row_align,
+                       int out_dtype, int32_t* topk_idx, float* topk_w,
+                       void* out, float* out_scales,
+                       int32_t* expert_counts, int32_t* expert_offsets,
+                       int32_t* group_offsets, int32_t* row_src, int32_t* dst_row,
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * moe_dispatch for callers that cannot allocate (code under HIP graph
@@ -179,8 +211,10 @@ int moe_dispatch(const void* x, const int32_t* topk_idx,
  *   MOE_EHIP if the scratch address cannot be obtained or a launch fails.
  * Every call on one GPU shares that GPU's array: calls that overlap on one
  * GPU (concurrent streams, or with a graph replay holding such a call) race
- * and give undefined results. Calls ordered on one stream are safe; each
- * call rewrites what it reads of the array before reading it.
+ * and give undefined results. Calls ordered on one stream are safe: the
+ * array is zero when the library is loaded, each call rewrites what it reads
+ * of it before reading it, and its control word returns to zero at the end
+ * of every call.
  */
 #define MOE_NO_ALLOC_SCRATCH_BYTES (16u << 20)
 

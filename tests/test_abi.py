@@ -57,10 +57,13 @@ def test_max_rows_and_workspace():
     assert lib.moe_dispatch_max_rows(10, 4, 2, 0) == -1          # row_align < 1
     assert lib.moe_dispatch_max_rows(10, 4, 2, 1025) == -1
     assert lib.moe_dispatch_max_rows(2 ** 28, 8, 8, 1) == -1     # rows overflow int32
-    # tile counts [tiles, E], then (256-byte aligned) in-tile ranks [T, k]
-    assert lib.moe_dispatch_workspace_bytes(16384, 256, 8, 32) == 64 * 256 * 4 + 16384 * 8 * 4
-    assert lib.moe_dispatch_workspace_bytes(300, 8, 2, 1) == 256 + 300 * 2 * 4
-    assert lib.moe_dispatch_workspace_bytes(0, 8, 2, 1) == 0
+    # 256 bytes of control (the ticket counter), tile counts [tiles, E], then
+    # (256-byte aligned) in-tile ranks [T, k]; tiles of 16 tokens up to
+    # T = 1024, 32 up to 4096, else 64
+    assert lib.moe_dispatch_workspace_bytes(16384, 256, 8, 32) == 256 + 256 * 256 * 4 + 16384 * 8 * 4
+    assert lib.moe_dispatch_workspace_bytes(4096, 384, 8, 1) == 256 + 128 * 384 * 4 + 4096 * 8 * 4
+    assert lib.moe_dispatch_workspace_bytes(300, 8, 2, 1) == 1024 + 300 * 2 * 4   # 19 tiles
+    assert lib.moe_dispatch_workspace_bytes(0, 8, 2, 1) == 256
     assert lib.moe_dispatch_workspace_bytes(300, 8, 2, 3) == 0   # E % groups != 0
 
 
@@ -74,7 +77,8 @@ def test_route_topk_validation():
     assert route(E=1025, k=2) == EINVAL
     assert route(T=-1) == EINVAL
     assert route(T=2 ** 31, k=2) == EINVAL
-    assert route(T=2 ** 27, E=256, k=8) == EINVAL        # one wave per token: 2^33 work-items
+    assert route(T=2 ** 27, E=1024, k=8) == EINVAL       # one wave per token: 2^33 work-items
+    assert route(T=2 ** 28, E=768, k=1) == EINVAL        # 16 lanes per token: 2^32 work-items
     assert route(logits=None) == ENULL
     assert route(idx=None) == ENULL
     assert route(logits=A + 2) == EALIGN
