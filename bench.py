@@ -2,16 +2,17 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3_prefill]
 
-One step = route (top-k) + dispatch (counts, scan, scatter/FP8) + combine
-over one batch of the workload's synthetic inputs, all resident in HBM. The
-stand-in experts run once before timing (they are not part of the path).
+One step = moe_route_dispatch (top-k, counts, scan, scatter/FP8) +
+moe_combine over one batch of the workload's synthetic inputs, all resident
+in HBM. The stand-in experts run once before timing (they are not part of
+the path).
 Before every step a 1 GiB scratch buffer is written so the step starts with
 a cold Infinity Cache; that write is outside the timed events. Dispatch and
 combine are timed with HIP events on the stream the kernels are launched on.
 
 Each timed step is bracketed by one pair of events (an event marker in the
-middle of the stream leaves a bubble of a few microseconds, so the per-part
-split is measured in a second pass with markers between the parts).
+middle of the stream leaves a bubble of a few microseconds, so the dispatch /
+combine split is measured in a second pass with a marker between the two).
 
 Prints one JSON line. value = effective HBM GB/s = algorithmic bytes of
 dispatch + combine / step time, median over steps.
@@ -80,9 +81,8 @@ def pct(a, q):
 def run_gpu(w, steps, warmup, cold=True, sender=False):
     import torch
 
-    from combine_moe_route_amd import (alloc_dispatch, moe_combine, moe_dispatch,
-                                       moe_dispatch_max_rows, moe_harness_expert_scale,
-                                       moe_route_topk)
+    from combine_moe_route_amd import (alloc_dispatch, moe_combine, moe_dispatch_max_rows,
+                                       moe_harness_expert_scale, moe_route_dispatch)
     from moe_synth import gen_inputs
 
     dev = torch.device("cuda:0")
@@ -98,8 +98,7 @@ def run_gpu(w, steps, warmup, cold=True, sender=False):
     scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
 
     # stand-in experts once (outside the path, untimed)
-    moe_route_topk(logits, w.k, topk_idx, topk_w)
-    moe_dispatch(x, topk_idx, w.E, w.groups, w.row_align, w.fp8, bufs)
+    moe_route_dispatch(logits, x, w.k, w.groups, w.row_align, w.fp8, bufs, topk_idx, topk_w)
     moe_harness_expert_scale(bufs, topk_idx, w.E, w.fp8, expert_out=expert_out)
     torch.cuda.synchronize()
     R = int(bufs.expert_offsets[-1].item())
@@ -107,44 +106,41 @@ def run_gpu(w, steps, warmup, cold=True, sender=False):
     stream = torch.cuda.current_stream(dev)
 
     def step(e=None, split=False):
-        # e: events [start, after route, after dispatch, end]; the inner two
-        # are recorded only when split is set, because every event marker
-        # leaves a few-microsecond bubble in the stream
+        # e: events [start, after dispatch, end]; the middle one is recorded
+        # only when split is set, because every event marker leaves a
+        # few-microsecond bubble in the stream
         if cold:
             scratch.fill_(1)
         if e is not None:
             e[0].record(stream)
-        moe_route_topk(logits, w.k, topk_idx, topk_w)
+        moe_route_dispatch(logits, x, w.k, w.groups, w.row_align, w.fp8, bufs, topk_idx, topk_w)
         if split:
             e[1].record(stream)
-        moe_dispatch(x, topk_idx, w.E, w.groups, w.row_align, w.fp8, bufs)
-        if split:
-            e[2].record(stream)
         moe_combine(expert_out, bufs.dst_row, topk_w, y)
         if e is not None:
-            e[3].record(stream)
+            e[2].record(stream)
 
     for _ in range(warmup):
         step()
     # timed steps: one event pair per step
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         step(ev[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    total = [a[0].elapsed_time(a[3]) * 1e3 for a in ev]           # microseconds
-    # split steps: route / dispatch / combine intervals (combine's interval is
-    # the combine kernel alone: its start marker follows dispatch's last kernel)
-    sp = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    total = [a[0].elapsed_time(a[2]) * 1e3 for a in ev]           # microseconds
+    # split steps: dispatch (route included) / combine intervals (combine's
+    # interval is the combine kernel alone: its start marker follows
+    # dispatch's last kernel)
+    sp = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     for i in range(steps):
         step(sp[i], split=True)
     torch.cuda.synchronize()
-    route = [a[0].elapsed_time(a[1]) * 1e3 for a in sp]
-    disp = [a[1].elapsed_time(a[2]) * 1e3 for a in sp]
-    comb = [a[2].elapsed_time(a[3]) * 1e3 for a in sp]
-    out = dict(R=R, total=total, route=route, disp=disp, comb=comb, wall_s=wall)
+    disp = [a[0].elapsed_time(a[1]) * 1e3 for a in sp]
+    comb = [a[1].elapsed_time(a[2]) * 1e3 for a in sp]
+    out = dict(R=R, total=total, disp=disp, comb=comb, wall_s=wall)
     if sender and w.groups > 1:
         out["sender"] = run_sender(w, steps, cold, scratch, stream, expert_out, bufs, topk_idx,
                                    topk_w, y)
@@ -279,9 +275,8 @@ def run_graph(w, steps):
     pair per replay with the 1 GiB write before it."""
     import torch
 
-    from combine_moe_route_amd import (alloc_dispatch, moe_combine, moe_dispatch,
-                                       moe_dispatch_max_rows, moe_harness_expert_scale,
-                                       moe_route_topk)
+    from combine_moe_route_amd import (alloc_dispatch, moe_combine, moe_dispatch_max_rows,
+                                       moe_harness_expert_scale, moe_route_dispatch)
     from moe_synth import gen_inputs
 
     dev = torch.device("cuda:0")
@@ -295,13 +290,11 @@ def run_graph(w, steps):
     expert_out = torch.empty((cap, w.H), dtype=torch.bfloat16, device=dev)
     y = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev)
     scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    moe_route_topk(logits, w.k, topk_idx, topk_w)
-    moe_dispatch(x, topk_idx, w.E, w.groups, w.row_align, w.fp8, bufs)
+    moe_route_dispatch(logits, x, w.k, w.groups, w.row_align, w.fp8, bufs, topk_idx, topk_w)
     moe_harness_expert_scale(bufs, topk_idx, w.E, w.fp8, expert_out=expert_out)
 
     def step():
-        moe_route_topk(logits, w.k, topk_idx, topk_w)
-        moe_dispatch(x, topk_idx, w.E, w.groups, w.row_align, w.fp8, bufs)
+        moe_route_dispatch(logits, x, w.k, w.groups, w.row_align, w.fp8, bufs, topk_idx, topk_w)
         moe_combine(expert_out, bufs.dst_row, topk_w, y)
 
     side = torch.cuda.Stream()
@@ -432,7 +425,7 @@ def cu_budget(w, steps, co="bf16"):
 
     from combine_moe_route_amd import (alloc_dispatch, moe_combine, moe_dispatch,
                                        moe_dispatch_max_rows, moe_harness_expert_scale,
-                                       moe_route_topk)
+                                       moe_route_dispatch, moe_route_topk)
     from moe_synth import gen_inputs
     hip = ctypes.CDLL("libamdhip64.so")
     dev = torch.device("cuda:0")
@@ -489,8 +482,7 @@ def cu_budget(w, steps, co="bf16"):
     torch.cuda.synchronize()
 
     def moe_step():
-        moe_route_topk(logits, w.k, idx, wt)
-        moe_dispatch(x, idx, w.E, w.groups, w.row_align, w.fp8, bufs)
+        moe_route_dispatch(logits, x, w.k, w.groups, w.row_align, w.fp8, bufs, idx, wt)
         moe_combine(eo, bufs.dst_row, wt, y)
 
     def gemm():
@@ -611,12 +603,11 @@ def cpu_baseline(w, max_tokens):
 def summarize(w, r):
     bd, bc = algorithmic_bytes(w.T, w.H, w.E, w.k, r["R"], w.fp8)
     tot = r["total"]
-    dmed = statistics.median([a + b for a, b in zip(r["route"], r["disp"])])
+    dmed = statistics.median(r["disp"])
     cmed = statistics.median(r["comb"])
     tmed = statistics.median(tot)
     return dict(
         bytes_dispatch=bd, bytes_combine=bc, rows=r["R"],
-        us_route=round(statistics.median(r["route"]), 2),
         us_dispatch=round(dmed, 2), us_combine=round(cmed, 2), us_total=round(tmed, 2),
         us_total_p10=round(pct(tot, 10), 2), us_total_p90=round(pct(tot, 90), 2),
         gbps=round((bd + bc) / (tmed * 1e-6) / 1e9, 1),
@@ -701,7 +692,7 @@ def main():
         print(f"[bench] {name} (decode, {args.decode_steps} steps)", file=sys.stderr, flush=True)
         cold_s = summarize(wd, run_gpu(wd, args.decode_steps, 20, cold=True))
         warm_s = summarize(wd, run_gpu(wd, args.decode_steps, 20, cold=False))
-        keys = ("us_route", "us_dispatch", "us_combine", "us_total", "us_total_p10",
+        keys = ("us_dispatch", "us_combine", "us_total", "us_total_p10",
                 "us_total_p90", "gbps")
         decode[name] = dict(rows=cold_s["rows"], bytes_total=cold_s["bytes_dispatch"] + cold_s["bytes_combine"],
                             cold={k: cold_s[k] for k in keys}, warm={k: warm_s[k] for k in keys},
@@ -728,7 +719,7 @@ def main():
         "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "k": w.k,
                    "groups": w.groups, "row_align": w.row_align,
                    "cache": "warm" if args.warm else "cold (1 GiB write before each step)"},
-        "us_dispatch": s["us_dispatch"], "us_route": s["us_route"],
+        "us_dispatch": s["us_dispatch"],
         "us_combine": s["us_combine"], "us_total": s["us_total"],
         "us_total_p10": s["us_total_p10"], "us_total_p90": s["us_total_p90"],
         "pct_of_peak": s["pct_of_peak"],

@@ -204,12 +204,11 @@ class DispatchBuffers(NamedTuple):
 def alloc_dispatch(T: int, H: int, E: int, k: int, groups: int = 1, row_align: int = 1,
                    fp8: bool = False, device="cuda", workspace: bool = True) -> DispatchBuffers:
     """Capacity-sized output buffers and workspace for moe_dispatch and
-    moe_route_dispatch (the workspace zero-filled, as the library requires
-    before its first use; a 4-byte placeholder when `workspace` is false, for
-    moe_dispatch_no_alloc)."""
+    moe_route_dispatch (a 16-byte placeholder workspace when `workspace` is
+    false, for moe_dispatch_no_alloc)."""
     dev = torch.device(device)
     R = moe_dispatch_max_rows(T, E, k, row_align)
-    ws = max(moe_dispatch_workspace_bytes(T, E, k, groups), 4) if workspace else 4
+    ws = max(moe_dispatch_workspace_bytes(T, E, k, groups), 16) if workspace else 16
     return DispatchBuffers(
         out=torch.empty((R, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev),
         out_scales=torch.empty((R, H // 128), dtype=torch.float32, device=dev) if fp8 else None,
@@ -218,7 +217,7 @@ def alloc_dispatch(T: int, H: int, E: int, k: int, groups: int = 1, row_align: i
         group_offsets=torch.empty(groups + 1, dtype=torch.int32, device=dev),
         row_src=torch.empty(R, dtype=torch.int32, device=dev),
         dst_row=torch.empty((T, k), dtype=torch.int32, device=dev),
-        workspace=torch.zeros(ws, dtype=torch.uint8, device=dev),
+        workspace=torch.empty(ws, dtype=torch.uint8, device=dev),
     )
 
 

@@ -152,11 +152,11 @@ int dispatch_impl(const float* logits, float* topk_w, const void* x, const int32
     a.dst_row = dst_row;
     const moe::DispatchWorkspace ws = moe::dispatch_workspace(T, E, k);
     unsigned char* wsb = static_cast<unsigned char*>(workspace);
-    a.ticket = reinterpret_cast<uint32_t*>(wsb);
-    a.tile_counts = reinterpret_cast<int32_t*>(wsb + ws.counts_off);
-    a.tile_rank = reinterpret_cast<int32_t*>(wsb + ws.rank_off);
+    a.tile_counts = wsb + ws.counts_off;
+    a.tile_base = reinterpret_cast<int32_t*>(wsb + ws.base_off);
+    a.tile_rank = wsb + ws.rank_off;
     a.max_rows = max_rows;
-    moe::LaunchInfo info[3];
+    moe::LaunchInfo info[4];
     int nk = 0;
     // geometry (route_sort_applies looks only at the logits address)
     (void)moe::launch_dispatch(a, nullptr, info, &nk, false);
@@ -171,19 +171,20 @@ int dispatch_impl(const float* logits, float* topk_w, const void* x, const int32
     if (!aligned(x, 16) || !aligned(out, 16)) return MOE_EALIGN;
     if (!aligned(topk_idx, 4) || !aligned(expert_counts, 4) || !aligned(expert_offsets, 4) ||
         !aligned(group_offsets, 4) || !aligned(row_src, 4) || !aligned(dst_row, 4) ||
-        !aligned(workspace, 4) || (fp8 && !aligned(out_scales, 4)))
+        !aligned(workspace, 16) || (fp8 && !aligned(out_scales, 4)))
         return MOE_EALIGN;
     if (route && (!aligned(logits, 4) || !aligned(topk_w, 4))) return MOE_EALIGN;
     // workspace
     if (workspace_bytes < ws.total) return MOE_ENOSPC;
-    if (!library_ws && !workspace) return MOE_ENULL;
+    if (!library_ws && ws.total > 0 && !workspace) return MOE_ENULL;
     if (!run) return MOE_OK;
 
     const hipError_t e = moe::launch_dispatch(a, stream, info, &nk);
     if (log_enabled())
         for (int i = 0; i < nk; i++)
-            log_launch(i == nk - 1 ? "dispatch.scatter"
-                       : i == nk - 2 ? (route && nk == 2 ? "dispatch.route_count" : "dispatch.count")
+            log_launch(i == nk - 1   ? "dispatch.scatter"
+                       : i == nk - 2 ? "dispatch.scan"
+                       : i == nk - 3 ? (route && nk == 3 ? "dispatch.route_count" : "dispatch.count")
                                      : "dispatch.route",
                        info[i]);
     return status_of(e);

@@ -12,59 +12,25 @@
 // inside every expert segment.
 //
 // Three kernels on the caller's stream:
-//   K2 k_tile_hist  one block per tile of 256 tokens. Each wave ORs its
-//                   lanes' bits into a per-wave 64-bit mask per expert in LDS
-//                   (atomic OR, so skewed experts do not serialise on a
-//                   counter). A token's rank within the tile for expert e is
-//                   the popcount of the lower lanes' bits plus the counts of
-//                   the earlier waves. Writes the tile's counts [tile, E] and
-//                   each slot's in-tile rank [T, k] (both in the workspace).
-//   K3 k_scan       one block. Per expert, an exclusive scan over tiles turns
-//                   tile counts into each tile's first row inside the segment
-//                   (this is what makes the order stable); totals are padded
-//                   to row_align and scanned over experts into offsets; group
-//                   offsets are read off the expert offsets. Several threads
-//                   share an expert, each scanning a contiguous tile range.
-//   K4 k_scatter    one wave per (token, row chunk): rows = segment offset +
-//                   tile base + in-tile rank; reads each x row once with
-//                   16-byte streaming loads and stores it to its k rows (FP8:
-//                   one quantisation per token, k stores); the chunk-0 wave
-//                   publishes dst_row / row_src. Leading blocks zero pad rows.
-#include "moe_device.h"
-#include "launch.h"
-
-// Dispatch: per-expert counts, segment offsets, and the stable scatter of
-// token rows into per-expert contiguous buffers (optionally FP8 with 1x128
-// scales).
-//
-// "Enabling trillion-parameter models on AWS EFA", Dispatch and Combine:
-// token counts per expert come first (accumulated with atomics in shared
-// memory), their cumulative sum gives the offsets at which tokens are packed
-// into contiguous per-expert send buffers. "Efficient and portable
-// mixture-of-experts communication", Dispatch: activations, block scales and
-// the token index are packed together; the receiver there fills its buffers
-// in a non-deterministic order, which this layout replaces with token order
-// inside every expert segment.
-//
-// Two launches on the caller's stream:
 //   count   one block per tile of TT tokens (TT = 16, 32 or 64 by T). The
 //           block ORs one bit per (token, slot) into a 64-bit mask per expert
-//           in LDS (atomic OR: a skewed expert costs no serialised counter),
-//           writes the tile's counts [tile, E] and, per slot, the token's rank
-//           within the tile for its expert (popcount of the lower tokens'
-//           bits). In moe_route_dispatch the same block first routes its
-//           tokens (top-k by sorting networks, topk_sort.h). Then it takes a
-//           ticket; the block that takes the last ticket (atomicInc wraps the
-//           counter back to zero for the next call) scans: per expert, an
-//           exclusive sum over tiles turns tile counts into each tile's first
-//           row inside the segment (this makes the order stable); totals are
-//           padded to row_align and summed over experts into offsets; group
-//           offsets are read off the expert offsets.
-//   scatter one wave per (token, row chunk): rows = tile base + in-tile rank;
-//           reads each x row once with 16-byte streaming loads and stores it
-//           to its k rows (FP8: one quantisation per token, k stores); the
-//           chunk-0 wave publishes dst_row / row_src. Leading blocks zero the
-//           pad rows.
+//           in LDS (atomic OR: a skewed expert costs no serialised counter)
+//           and writes the tile's counts [tile, E] and, per slot, the token's
+//           rank within the tile for its expert (popcount of the lower
+//           tokens' bits). Both fit a byte: at most 64 tokens per tile. In
+//           moe_route_dispatch the same block first routes its tokens (top-k
+//           by sorting networks, topk_sort.h).
+//   scan    one block. The byte counts come into LDS in one batch of 16-byte
+//           loads (in chunks when they exceed 64 KiB); per expert an exclusive
+//           sum over tiles gives each tile's first row inside the expert's
+//           segment (this makes the order stable); the totals, padded to
+//           row_align, are summed over experts into offsets; group offsets are
+//           read off the expert offsets.
+//   scatter one wave per (token, row chunk): row = segment offset + tile prefix
+//           + in-tile rank; reads each x row once with 16-byte streaming loads
+//           and stores it to its k rows (FP8: one quantisation per token, k
+//           stores); the chunk-0 wave publishes dst_row / row_src. Leading
+//           blocks zero the pad rows.
 #include "moe_device.h"
 #include "launch.h"
 #include "topk_sort.h"
@@ -78,33 +44,32 @@ int64_t dispatch_tiles(int64_t T) {
     return (T + TT - 1) / TT;
 }
 
+static size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+
+static int count_row_bytes(int E) { return (E + 3) & ~3; }
+
 DispatchWorkspace dispatch_workspace(int64_t T, int E, int k) {
     DispatchWorkspace w;
     w.tile_tokens = dispatch_tile_tokens(T);
     w.tiles = dispatch_tiles(T);
-    w.counts_off = 256;   // [0, 256): the ticket counter (word 0)
-    const size_t counts = (size_t)w.tiles * (size_t)E * sizeof(int32_t);
-    w.rank_off = (w.counts_off + counts + 255) / 256 * 256;
-    w.total = w.rank_off + (size_t)T * (size_t)k * sizeof(int32_t);
+    w.counts_off = 0;
+    w.base_off = round256((size_t)w.tiles * (size_t)count_row_bytes(E));
+    w.rank_off = w.base_off + round256((size_t)w.tiles * (size_t)E * sizeof(int32_t));
+    w.total = w.rank_off + round256((size_t)T * (size_t)k);
     return w;
-}
-
-static int pow2_at_least(int n) {
-    int p = 1;
-    while (p < n) p <<= 1;
-    return p;
 }
 
 // ---------------------------------------------------------------- count
 
 // Tile histogram and in-tile ranks. ids(p) is the expert of pair p = tl * k + j
 // of the tile (token tl, slot j), npairs = tokens in the tile * k. Writes the
-// tile's counts tile_counts[tile * E + e] and rank[p] (the tile's slice of the
-// [T, k] rank array; -1 for a slot whose expert is outside [0, E)).
+// tile's counts counts[e] (the row padded with zeros to a multiple of 4
+// bytes) and rank[p] (the tile's slice of the [T, k] rank array; 0xFF for a
+// slot whose expert is outside [0, E), which the scatter never reads).
 template <typename Ids>
-__device__ __forceinline__ void count_tile(Ids ids, int npairs, int k, int E, int64_t tile,
-                                           uint64_t* s_mask, int32_t* __restrict__ tile_counts,
-                                           int32_t* __restrict__ rank) {
+__device__ __forceinline__ void count_tile(Ids ids, int npairs, int k, int E, uint64_t* s_mask,
+                                           uint8_t* __restrict__ counts,
+                                           uint8_t* __restrict__ rank) {
     const int NT = blockDim.x;
     const int tid = threadIdx.x;
     for (int i = tid; i < E; i += NT) s_mask[i] = 0ull;
@@ -114,12 +79,89 @@ __device__ __forceinline__ void count_tile(Ids ids, int npairs, int k, int E, in
         if ((unsigned)e < (unsigned)E) atomicOr(&s_mask[e], 1ull << (p / k));
     }
     __syncthreads();
-    for (int i = tid; i < E; i += NT) tile_counts[tile * E + i] = __popcll(s_mask[i]);
+    for (int i = tid; i < ((E + 3) & ~3); i += NT)
+        counts[i] = i < E ? (uint8_t)__popcll(s_mask[i]) : (uint8_t)0;
     for (int p = tid; p < npairs; p += NT) {
         const int e = ids(p);
-        int r = -1;
+        int r = 0xFF;
         if ((unsigned)e < (unsigned)E) r = __popcll(s_mask[e] & ((1ull << (p / k)) - 1ull));
-        rank[p] = r;
+        rank[p] = (uint8_t)r;
+    }
+}
+
+struct CountArgs {
+    int64_t T;
+    int E, k, TT;
+    int64_t tiles;
+    uint8_t* tile_counts;   // [tiles, E]
+    uint8_t* tile_rank;     // [T, k]
+};
+
+// Counts from a given routing table [T, k]: one block per tile.
+__global__ __launch_bounds__(1024) void k_count(const int32_t* __restrict__ topk_idx,
+                                                CountArgs a) {
+    extern __shared__ uint64_t s_mask[];   // [E]
+    const int64_t tile = blockIdx.x;
+    const int64_t t0 = tile * a.TT;
+    const int n = (int)min((int64_t)a.TT, a.T - t0);
+    const int32_t* ids = topk_idx + t0 * a.k;
+    count_tile([ids](int p) { return ids[p]; }, n * a.k, a.k, a.E, s_mask,
+               a.tile_counts + tile * ((a.E + 3) & ~3), a.tile_rank + t0 * a.k);
+}
+
+// Route + count: the tile's TT tokens are routed first by TT * S threads (S
+// lanes per token), their experts kept in LDS for the count.
+template <int S, int K>
+__global__ __launch_bounds__(1024) void k_route_count(const float* __restrict__ logits,
+                                                      int32_t* __restrict__ topk_idx,
+                                                      float* __restrict__ topk_w, CountArgs a) {
+    extern __shared__ uint64_t s_mask[];   // [E], then the tile's experts [TT * k]
+    int32_t* s_ids = reinterpret_cast<int32_t*>(s_mask + a.E);
+    const int64_t tile = blockIdx.x;
+    const int64_t t0 = tile * a.TT;
+    const int n = (int)min((int64_t)a.TT, a.T - t0);
+    if ((int)threadIdx.x < a.TT * S) {   // whole lane groups
+        const int tl = threadIdx.x / S;
+        const int g = threadIdx.x & (S - 1);
+        const int64_t t = t0 + tl;
+        const bool live = tl < n;
+        double list[K];
+        route_token<S, K>(logits + (live ? t : 0) * (int64_t)a.E, live, a.E, g, list);
+        if (live)
+            write_route<S, K>(list, g, t, tl, a.E, a.k, a.k, 0, 0.0f, topk_idx, topk_w, s_ids);
+    }
+    __syncthreads();
+    count_tile([s_ids](int p) { return s_ids[p]; }, n * a.k, a.k, a.E, s_mask,
+               a.tile_counts + tile * ((a.E + 3) & ~3), a.tile_rank + t0 * a.k);
+}
+
+// ---------------------------------------------------------------- scan
+
+constexpr int kScanThreads = 1024;
+constexpr int kScanLdsBytes = 64 * 1024;   // byte counts staged per chunk
+
+// Byte i of word w.
+__device__ __forceinline__ int byte_of(uint32_t w, int i) { return (int)((w >> (8 * i)) & 0xFFu); }
+
+// Adds to acc[0..3] the columns 4q .. 4q+3 of rows [r0, r1) of the staged byte
+// counts (one 32-bit word per row and column group, Q words per row),
+// reading 8 rows at a time so that the LDS reads are in flight together.
+__device__ __forceinline__ void column_sum4(const uint32_t* s_cnt, int r0, int r1, int Q, int q,
+                                            int acc[4]) {
+    int r = r0;
+    for (; r + 8 <= r1; r += 8) {
+        uint32_t w[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) w[i] = s_cnt[(r + i) * Q + q];
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+#pragma unroll
+            for (int b = 0; b < 4; b++) acc[b] += byte_of(w[i], b);
+    }
+    for (; r < r1; r++) {
+        const uint32_t w = s_cnt[r * Q + q];
+#pragma unroll
+        for (int b = 0; b < 4; b++) acc[b] += byte_of(w, b);
     }
 }
 
@@ -133,177 +175,190 @@ __device__ __forceinline__ int wave_inclusive_sum(int v) {
     return v;
 }
 
-// True in every thread of the block that finishes last. Each block's global
-// writes are released (device-scope fence) before it takes its ticket; the
-// last block acquires before it reads what the others wrote. atomicInc wraps
-// the counter to zero on the last ticket, ready for the next launch.
-__device__ __forceinline__ bool last_block(uint32_t* ticket) {
-    __shared__ int s_last;
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) s_last = atomicInc(ticket, gridDim.x - 1) == gridDim.x - 1;
-    __syncthreads();
-    const bool last = s_last != 0;
-    if (last) __threadfence();
-    return last;
-}
+// Up to kScanBlocks blocks of 1024 threads. Thread tid = p * Qp + q handles
+// the four experts 4q .. 4q+3 (Q = ceil(E / 4) groups, Qp = Q rounded up to a
+// power of two), P = min(1024 / Qp, 16) threads sharing a group (the rest
+// only take part in the expert scan). Every block reads all
+// byte counts (into LDS, in chunks of 64 KiB) and computes every expert's
+// total and, for its own range of tiles, every expert's prefix at the range
+// start; every block then scans the padded totals over experts (the same
+// offsets in each block; block 0 writes them). Each block writes the tile
+// prefixes (relative to the segment start) of its own range only, so the
+// stores spread over the blocks and no block waits for another.
+constexpr int kScanBlocks = 32;
+constexpr int kScanShare = 16;   // at most this many threads per expert group
 
-constexpr int kScanBatch = 16;
-
-// Scan over tiles by one block of NT >= Ep threads (Ep = E rounded up to a
-// power of two), laid out as tid = p * Ep + e: P = NT / Ep threads share
-// expert e, thread p owning a contiguous range of tiles. Pass 1 sums each
-// range with batches of independent loads; an LDS exchange gives each range
-// its start inside the expert's segment; the p == 0 threads (tid 0 .. Ep-1,
-// in expert order) scan the padded totals over experts; pass 2 rewrites the
-// tile counts as tile bases (segment offset + rows of earlier tiles).
-__device__ void scan_tiles(int32_t* __restrict__ tile_counts, int64_t tiles, int E, int row_align,
-                           int groups, int32_t* __restrict__ expert_counts,
-                           int32_t* __restrict__ expert_offsets,
-                           int32_t* __restrict__ group_offsets) {
-    __shared__ int32_t s_part[1024];
+__global__ __launch_bounds__(kScanThreads) void k_scan(const uint8_t* __restrict__ tile_counts,
+                                                       int64_t tiles, int E, int row_align,
+                                                       int groups,
+                                                       int32_t* __restrict__ tile_base,
+                                                       int32_t* __restrict__ expert_counts,
+                                                       int32_t* __restrict__ expert_offsets,
+                                                       int32_t* __restrict__ group_offsets) {
+    __shared__ __align__(16) uint32_t s_cnt[kScanLdsBytes / 4];
+    __shared__ int32_t s_all[4][kScanThreads];
+    __shared__ int32_t s_pre[4][kScanThreads];
     __shared__ int32_t s_off[kMaxExperts + 1];
-    __shared__ int32_t s_wave[1024 / kWave];
+    __shared__ int32_t s_wave[kScanThreads / kWave];
 
-    const int NT = blockDim.x;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
-    int Ep = 1;
-    while (Ep < E) Ep <<= 1;
-    const int P = NT / Ep;
-    const int e = tid & (Ep - 1);
-    const int p = tid / Ep;
-    const bool real = e < E;
-    const int64_t per = (tiles + P - 1) / P;
-    const int64_t b0 = min(tiles, (int64_t)p * per);
-    const int64_t b1 = min(tiles, b0 + per);
+    const int E4 = (E + 3) & ~3;   // bytes per count row
+    const int Q = E4 / 4;
+    int Qp = 1;
+    while (Qp < Q) Qp <<= 1;
+    const int P = kScanThreads / Qp < kScanShare ? kScanThreads / Qp : kScanShare;
+    const int q = tid & (Qp - 1);
+    const int p = tid / Qp;
+    const bool real = q < Q && p < P;
+    // this block's tiles
+    const int64_t per_block = (tiles + gridDim.x - 1) / gridDim.x;
+    const int64_t my0 = min(tiles, (int64_t)blockIdx.x * per_block);
+    const int64_t my1 = min(tiles, my0 + per_block);
+    // tiles per chunk: a multiple of 16, so every chunk starts 16-byte aligned
+    const int64_t chunk = (int64_t)(kScanLdsBytes / E4) / 16 * 16;
 
-    int part = 0;
-    if (real) {
-        for (int64_t b = b0; b < b1; b += kScanBatch) {
-            int c[kScanBatch];
+    // stage tiles [c0, c0 + nt) of the byte counts; c0 is a multiple of 16,
+    // so the source is 16-byte aligned, and the count array is padded to 256
+    // bytes, so rounding the length up to 16 stays inside it (every load of
+    // the chunk is issued before the first LDS store)
+    auto stage = [&](int64_t c0, int nt) {
+        constexpr int kIters = kScanLdsBytes / (16 * kScanThreads);
+        const int n16 = (nt * E4 + 15) / 16;
+        const uint4* src = reinterpret_cast<const uint4*>(tile_counts + c0 * E4);
+        uint4* dst = reinterpret_cast<uint4*>(s_cnt);
+        uint4 v[kIters];
 #pragma unroll
-            for (int i = 0; i < kScanBatch; i++)
-                c[i] = (b + i < b1) ? tile_counts[(b + i) * E + e] : 0;
-#pragma unroll
-            for (int i = 0; i < kScanBatch; i++) part += c[i];
+        for (int j = 0; j < kIters; j++) {
+            const int i = tid + j * kScanThreads;
+            v[j] = i < n16 ? src[i] : make_uint4(0u, 0u, 0u, 0u);
         }
+#pragma unroll
+        for (int j = 0; j < kIters; j++) {
+            const int i = tid + j * kScanThreads;
+            if (i < n16) dst[i] = v[j];
+        }
+    };
+
+    // pass 1: totals and the prefix at my0, over all tiles
+    int all[4] = {0, 0, 0, 0}, pre[4] = {0, 0, 0, 0};
+    int64_t last_c0 = 0;
+    int last_nt = 0;   // the chunk left in LDS
+    for (int64_t c0 = 0; c0 < tiles; c0 += chunk) {
+        const int nt = (int)min(chunk, tiles - c0);
+        __syncthreads();
+        stage(c0, nt);
+        __syncthreads();
+        const int per = (nt + P - 1) / P;
+        const int r0 = min(nt, p * per);
+        const int r1 = min(nt, r0 + per);
+        if (real) {
+            column_sum4(s_cnt, r0, r1, Q, q, all);
+            const int64_t before_mine = my0 - c0;   // rows of this chunk before my0
+            if (before_mine > r0)
+                column_sum4(s_cnt, r0, (int)min((int64_t)r1, before_mine), Q, q, pre);
+        }
+        last_c0 = c0;
+        last_nt = nt;
     }
-    s_part[tid] = part;
+    const bool staged_mine = last_c0 <= my0 && my1 <= last_c0 + last_nt;
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+        s_all[b][tid] = all[b];
+        s_pre[b][tid] = pre[b];
+    }
     __syncthreads();
-    int before = 0, cnt = 0;
-    for (int q = 0; q < P; q++) {
-        const int v = s_part[q * Ep + e];
-        before += q < p ? v : 0;
-        cnt += v;
-    }
-    const int padded = (p == 0 && real) ? (cnt + row_align - 1) / row_align * row_align : 0;
+    int cnt[4] = {0, 0, 0, 0}, start[4] = {0, 0, 0, 0};
+    if (real)
+        for (int pp = 0; pp < P; pp++)
+#pragma unroll
+            for (int b = 0; b < 4; b++) {
+                cnt[b] += s_all[b][pp * Qp + q];
+                start[b] += s_pre[b][pp * Qp + q];
+            }
+    int padded[4];
+#pragma unroll
+    for (int b = 0; b < 4; b++)
+        padded[b] = (p == 0 && real && 4 * q + b < E)
+                        ? (cnt[b] + row_align - 1) / row_align * row_align : 0;
+    const int mine = padded[0] + padded[1] + padded[2] + padded[3];
 
     // exclusive scan of the padded totals over experts (only the p == 0
     // threads contribute; they come first, in expert order)
-    const int incl = wave_inclusive_sum(padded);
+    const int incl = wave_inclusive_sum(mine);
     if (lane == kWave - 1) s_wave[wave] = incl;
     __syncthreads();
     if (wave == 0) {
-        const int v = lane < NT / kWave ? s_wave[lane] : 0;
+        const int v = lane < kScanThreads / kWave ? s_wave[lane] : 0;
         const int vi = wave_inclusive_sum(v);
-        if (lane < NT / kWave) s_wave[lane] = vi - v;
+        if (lane < kScanThreads / kWave) s_wave[lane] = vi - v;
     }
     __syncthreads();
-    const int excl = s_wave[wave] + incl - padded;
     if (p == 0 && real) {
-        expert_counts[e] = cnt;
-        expert_offsets[e] = excl;
-        s_off[e] = excl;
-        if (e == E - 1) {
-            expert_offsets[E] = excl + padded;
-            s_off[E] = excl + padded;
+        int off = s_wave[wave] + incl - mine;
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+            const int e = 4 * q + b;
+            if (e < E) {
+                s_off[e] = off;
+                if (blockIdx.x == 0) {
+                    expert_counts[e] = cnt[b];
+                    expert_offsets[e] = off;
+                }
+                off += padded[b];
+                if (e == E - 1) {
+                    s_off[E] = off;
+                    if (blockIdx.x == 0) expert_offsets[E] = off;
+                }
+            }
         }
     }
     __syncthreads();
-    if (group_offsets != nullptr)
-        for (int gi = tid; gi <= groups; gi += NT) group_offsets[gi] = s_off[gi * (E / groups)];
+    if (blockIdx.x == 0 && group_offsets != nullptr)
+        for (int gi = tid; gi <= groups; gi += kScanThreads)
+            group_offsets[gi] = s_off[gi * (E / groups)];
 
-    if (real) {
-        int run = s_off[e] + before;
-        for (int64_t b = b0; b < b1; b += kScanBatch) {
-            int c[kScanBatch];
-#pragma unroll
-            for (int i = 0; i < kScanBatch; i++)
-                c[i] = (b + i < b1) ? tile_counts[(b + i) * E + e] : 0;
-#pragma unroll
-            for (int i = 0; i < kScanBatch; i++)
-                if (b + i < b1) {
-                    tile_counts[(b + i) * E + e] = run;
-                    run += c[i];
-                }
+    // pass 2: the prefixes of my tiles. The P threads of a group split each
+    // staged piece: thread p takes rows [r0, r1) and adds the rows before
+    // them from LDS; every thread carries the piece's total into the next.
+    int run[4] = {start[0], start[1], start[2], start[3]};
+    int64_t c0 = my0;
+    while (c0 < my1) {
+        int64_t s0 = last_c0;   // staged range [s0, s0 + snt)
+        int snt = last_nt;
+        if (!staged_mine) {
+            s0 = c0 & ~(int64_t)15;
+            snt = (int)min(chunk, tiles - s0);
+            __syncthreads();
+            stage(s0, snt);
+            __syncthreads();
         }
-    }
-}
-
-struct CountArgs {
-    int64_t T;
-    int E, k, TT, row_align, groups;
-    int64_t tiles;
-    uint32_t* ticket;
-    int32_t* tile_counts;
-    int32_t* tile_rank;
-    int32_t* expert_counts;
-    int32_t* expert_offsets;
-    int32_t* group_offsets;
-};
-
-// Count + scan from a given routing table [T, k]. One block per tile (at
-// least one block, which then only scans: T == 0 writes zero counts).
-__global__ __launch_bounds__(1024) void k_count(const int32_t* __restrict__ topk_idx,
-                                                CountArgs a) {
-    extern __shared__ uint64_t s_mask[];   // [E]
-    const int64_t tile = blockIdx.x;
-    if (tile < a.tiles) {
-        const int64_t t0 = tile * a.TT;
-        const int n = (int)min((int64_t)a.TT, a.T - t0);
-        const int32_t* ids = topk_idx + t0 * a.k;
-        count_tile([ids](int p) { return ids[p]; }, n * a.k, a.k, a.E, tile, s_mask,
-                   a.tile_counts, a.tile_rank + t0 * a.k);
-    }
-    if (last_block(a.ticket))
-        scan_tiles(a.tile_counts, a.tiles, a.E, a.row_align, a.groups, a.expert_counts,
-                   a.expert_offsets, a.group_offsets);
-}
-
-// Route + count + scan: the tile's TT tokens are routed first by TT * S
-// threads (S lanes per token), their experts kept in LDS for the count.
-template <int S, int K>
-__global__ __launch_bounds__(1024) void k_route_count(const float* __restrict__ logits,
-                                                      int32_t* __restrict__ topk_idx,
-                                                      float* __restrict__ topk_w, CountArgs a) {
-    extern __shared__ uint64_t s_mask[];   // [E], then the tile's experts [TT * k]
-    int32_t* s_ids = reinterpret_cast<int32_t*>(s_mask + a.E);
-    const int64_t tile = blockIdx.x;
-    if (tile < a.tiles) {
-        const int64_t t0 = tile * a.TT;
-        const int n = (int)min((int64_t)a.TT, a.T - t0);
-        if ((int)threadIdx.x < a.TT * S) {   // whole lane groups
-            const int tl = threadIdx.x / S;
-            const int g = threadIdx.x & (S - 1);
-            const int64_t t = t0 + tl;
-            const bool live = tl < n;
-            double list[K];
-            route_token<S, K>(logits + (live ? t : 0) * (int64_t)a.E, live, a.E, g, list);
-            if (live)
-                write_route<S, K>(list, g, t, tl, a.E, a.k, a.k, 0, 0.0f, topk_idx, topk_w, s_ids);
+        const int nt = (int)min(my1 - c0, s0 + snt - c0);
+        const int sr0 = (int)(c0 - s0);
+        const int per = (nt + P - 1) / P;
+        const int r0 = min(nt, p * per);
+        const int r1 = min(nt, r0 + per);
+        if (real) {
+            int v[4] = {run[0], run[1], run[2], run[3]};
+            column_sum4(s_cnt, sr0, sr0 + r0, Q, q, v);
+            for (int r = r0; r < r1; r++) {
+                const uint32_t w = s_cnt[(sr0 + r) * Q + q];
+                int32_t* dst = tile_base + (c0 + r) * E + 4 * q;
+#pragma unroll
+                for (int b = 0; b < 4; b++)
+                    if (4 * q + b < E) {
+                        dst[b] = v[b];
+                        v[b] += byte_of(w, b);
+                    }
+            }
+            column_sum4(s_cnt, sr0, sr0 + nt, Q, q, run);
         }
-        __syncthreads();
-        count_tile([s_ids](int p) { return s_ids[p]; }, n * a.k, a.k, a.E, tile, s_mask,
-                   a.tile_counts, a.tile_rank + t0 * a.k);
+        c0 += nt;
     }
-    if (last_block(a.ticket))
-        scan_tiles(a.tile_counts, a.tiles, a.E, a.row_align, a.groups, a.expert_counts,
-                   a.expert_offsets, a.group_offsets);
 }
 
-// ---------------------------------------------------------------- K4
+// ---------------------------------------------------------------- scatter
 
 constexpr int kScatterThreads = 256;
 
@@ -342,10 +397,11 @@ __device__ void zero_pad_rows(int pb, int pad_blocks_per_expert, int pad_rows_pe
 
 constexpr int kScatterWaves = kScatterThreads / kWave;
 
-// Destination rows of slots j0 .. j0+7 of token t: segment offset + tile's
-// first row in the segment (tile_base) + in-tile rank; -1 for dropped slots.
+// Destination rows of slots j0 .. j0+7 of token t: the segment offset + the
+// tile's first row in the segment (tb) + in-tile rank; -1 for dropped slots.
 __device__ __forceinline__ void slot_rows(const int32_t* __restrict__ topk_idx,
-                                          const int32_t* __restrict__ tile_rank,
+                                          const uint8_t* __restrict__ tile_rank,
+                                          const int32_t* __restrict__ offsets,
                                           const int32_t* __restrict__ tb, int64_t p0, int j0,
                                           int k, int E, int64_t max_rows, int r[8]) {
 #pragma unroll
@@ -354,7 +410,7 @@ __device__ __forceinline__ void slot_rows(const int32_t* __restrict__ topk_idx,
         if (j0 + jj < k) {
             const int e = topk_idx[p0 + j0 + jj];
             if ((unsigned)e < (unsigned)E) {
-                const int rr = tb[e] + tile_rank[p0 + j0 + jj];
+                const int rr = offsets[e] + tb[e] + tile_rank[p0 + j0 + jj];
                 r[jj] = (rr < 0 || rr >= max_rows) ? -1 : rr;   // never write outside
             }
         }
@@ -381,7 +437,7 @@ __device__ __forceinline__ void publish_rows(int lane, int64_t p0, int j0, int k
 // token's rows.
 __global__ __launch_bounds__(kScatterThreads) void k_scatter_bf16(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ topk_idx,
-    const int32_t* __restrict__ tile_rank, const int32_t* __restrict__ tile_base,
+    const uint8_t* __restrict__ tile_rank, const int32_t* __restrict__ tile_base,
     const int32_t* __restrict__ expert_counts, const int32_t* __restrict__ expert_offsets,
     int64_t T, int H, int E, int k, int TT, int64_t max_rows, int pad_blocks,
     int pad_blocks_per_expert, int pad_rows_per_block, unsigned char* __restrict__ out,
@@ -406,7 +462,7 @@ __global__ __launch_bounds__(kScatterThreads) void k_scatter_bf16(
     const int32_t* tb = tile_base + (t / TT) * E;
     for (int j0 = 0; j0 < k; j0 += 8) {
         int r[8];
-        slot_rows(topk_idx, tile_rank, tb, p0, j0, k, E, max_rows, r);
+        slot_rows(topk_idx, tile_rank, expert_offsets, tb, p0, j0, k, E, max_rows, r);
         if (chunk == 0) publish_rows(lane, p0, j0, k, r, dst_row, row_src);
         if (u < U) {
 #pragma unroll
@@ -426,7 +482,7 @@ __global__ __launch_bounds__(kScatterThreads) void k_scatter_bf16(
 // pieces from different waves, which cost HBM read-modify-write cycles).
 __global__ __launch_bounds__(1024) void k_scatter_fp8(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ topk_idx,
-    const int32_t* __restrict__ tile_rank, const int32_t* __restrict__ tile_base,
+    const uint8_t* __restrict__ tile_rank, const int32_t* __restrict__ tile_base,
     const int32_t* __restrict__ expert_counts, const int32_t* __restrict__ expert_offsets,
     int64_t T, int H, int E, int k, int TT, int64_t max_rows, int pad_blocks,
     int pad_blocks_per_expert, int pad_rows_per_block, unsigned char* __restrict__ out,
@@ -470,7 +526,7 @@ __global__ __launch_bounds__(1024) void k_scatter_fp8(
         if (u < U && (u & 7) == 0) s_scale[u >> 3] = s;
         for (int j0 = 0; j0 < k; j0 += 8) {
             int r[8];
-            slot_rows(topk_idx, tile_rank, tb, p0, j0, k, E, max_rows, r);
+            slot_rows(topk_idx, tile_rank, expert_offsets, tb, p0, j0, k, E, max_rows, r);
             if (chunk == 0) publish_rows(lane, p0, j0, k, r, dst_row, row_src);
             if (u < U) {
 #pragma unroll
@@ -485,7 +541,7 @@ __global__ __launch_bounds__(1024) void k_scatter_fp8(
     for (int j = w; j < k; j += W) {
         const int e = topk_idx[p0 + j];
         if ((unsigned)e >= (unsigned)E) continue;
-        const int rr = tb[e] + tile_rank[p0 + j];
+        const int rr = expert_offsets[e] + tb[e] + tile_rank[p0 + j];
         if (rr < 0 || rr >= max_rows) continue;
         for (int i = lane; i < nb; i += kWave) scales[(int64_t)rr * nb + i] = s_scale[i];
     }
@@ -512,22 +568,20 @@ static void launch_route_count_k(int S, const DispatchArgs& a, const CountArgs& 
     }
 }
 
-hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream, LaunchInfo info[3], int* n,
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream, LaunchInfo info[4], int* n,
                            bool run) {
     const DispatchWorkspace ws = dispatch_workspace(a.T, a.E, a.k);
     const int TT = ws.tile_tokens;
     const int64_t tiles = ws.tiles;
-    const int Ep = pow2_at_least(a.E);
     // routing inside the count kernel when the sorting-network path applies
     const bool fused = a.logits != nullptr && route_sort_applies(a.logits, a.E, a.k);
     const bool route_first = a.logits != nullptr && !fused;
-    const int S = fused ? route_lanes(a.E) : 1;
+    const int S = fused ? route_lanes(a.T, a.E) : 1;
     int count_threads = fused ? TT * S : 256;
-    if (count_threads < Ep) count_threads = Ep;
     if (count_threads < kWave) count_threads = kWave;
     const size_t count_lds = (size_t)a.E * sizeof(uint64_t) +
                              (fused ? (size_t)TT * a.k * sizeof(int32_t) : 0);
-    const int64_t count_grid = tiles > 0 ? tiles : 1;
+    const int64_t scan_blocks = tiles < 1 ? 1 : tiles < kScanBlocks ? tiles : kScanBlocks;
 
     int pad_per_expert = 0, pad_rows_per_block = 0;
     if (a.row_align > 1 && a.T > 0) {
@@ -550,12 +604,13 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream, LaunchInfo
                                 a.topk_w, stream, &route_info, false);
     if (info) {
         if (route_first) info[nk++] = route_info;
-        info[nk++] = LaunchInfo{count_grid, count_threads, count_lds, fused ? S : TT};
+        info[nk++] = LaunchInfo{tiles, count_threads, count_lds, fused ? S : TT};
+        info[nk++] = LaunchInfo{scan_blocks, kScanThreads, 0, tiles};
         info[nk++] = a.fp8 ? LaunchInfo{scatter_blocks, fp8_threads,
                                         (size_t)(a.H / 128) * sizeof(float), fp8_waves}
                            : LaunchInfo{scatter_blocks, kScatterThreads, 0, bf16_waves_per_token};
     } else {
-        nk = route_first ? 3 : 2;
+        nk = route_first ? 4 : 3;
     }
     if (n) *n = nk;
     if (!run) return hipSuccess;
@@ -566,18 +621,22 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream, LaunchInfo
                                 a.topk_w, stream, nullptr);
         if (err != hipSuccess) return err;
     }
-    const CountArgs c{a.T, a.E, a.k, TT, a.row_align, a.groups, tiles, a.ticket, a.tile_counts,
-                      a.tile_rank, a.expert_counts, a.expert_offsets, a.group_offsets};
-    if (fused) {
-        switch (route_list_len(a.k)) {
-            case 2: launch_route_count_k<2>(S, a, c, count_grid, count_threads, count_lds, stream); break;
-            case 4: launch_route_count_k<4>(S, a, c, count_grid, count_threads, count_lds, stream); break;
-            default: launch_route_count_k<8>(S, a, c, count_grid, count_threads, count_lds, stream); break;
+    const CountArgs c{a.T, a.E, a.k, TT, tiles, a.tile_counts, a.tile_rank};
+    if (tiles > 0) {
+        if (fused) {
+            switch (route_list_len(a.k)) {
+                case 2: launch_route_count_k<2>(S, a, c, tiles, count_threads, count_lds, stream); break;
+                case 4: launch_route_count_k<4>(S, a, c, tiles, count_threads, count_lds, stream); break;
+                default: launch_route_count_k<8>(S, a, c, tiles, count_threads, count_lds, stream); break;
+            }
+        } else {
+            k_count<<<dim3((unsigned)tiles), dim3(count_threads), count_lds, stream>>>(a.topk_idx, c);
         }
-    } else {
-        k_count<<<dim3((unsigned)count_grid), dim3(count_threads), count_lds, stream>>>(a.topk_idx,
-                                                                                        c);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
     }
+    k_scan<<<dim3((unsigned)scan_blocks), kScanThreads, 0, stream>>>(
+        a.tile_counts, tiles, a.E, a.row_align, a.groups, a.tile_base, a.expert_counts,
+        a.expert_offsets, a.group_offsets);
     if ((err = hipGetLastError()) != hipSuccess) return err;
 
     // scatter: leading blocks zero pad rows, then the token work
@@ -587,14 +646,14 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream, LaunchInfo
     if (a.fp8) {
         const size_t lds = (size_t)(a.H / 128) * sizeof(float);
         k_scatter_fp8<<<dim3((unsigned)scatter_blocks), dim3(fp8_threads), lds, stream>>>(
-            x, a.topk_idx, a.tile_rank, a.tile_counts, a.expert_counts, a.expert_offsets, a.T,
-            a.H, a.E, a.k, TT, a.max_rows, (int)pad_blocks, pad_per_expert, pad_rows_per_block,
-            out, a.out_scales, a.row_src, a.dst_row);
+            x, a.topk_idx, a.tile_rank, a.tile_base, a.expert_counts, a.expert_offsets, a.T, a.H,
+            a.E, a.k, TT, a.max_rows, (int)pad_blocks, pad_per_expert, pad_rows_per_block, out,
+            a.out_scales, a.row_src, a.dst_row);
     } else {
         k_scatter_bf16<<<dim3((unsigned)scatter_blocks), dim3(kScatterThreads), 0, stream>>>(
-            x, a.topk_idx, a.tile_rank, a.tile_counts, a.expert_counts, a.expert_offsets, a.T,
-            a.H, a.E, a.k, TT, a.max_rows, (int)pad_blocks, pad_per_expert, pad_rows_per_block,
-            out, a.row_src, a.dst_row);
+            x, a.topk_idx, a.tile_rank, a.tile_base, a.expert_counts, a.expert_offsets, a.T, a.H,
+            a.E, a.k, TT, a.max_rows, (int)pad_blocks, pad_per_expert, pad_rows_per_block, out,
+            a.row_src, a.dst_row);
     }
     return hipGetLastError();
 }

@@ -51,29 +51,32 @@ struct DispatchArgs {
     int32_t* group_offsets;
     int32_t* row_src;
     int32_t* dst_row;
-    uint32_t* ticket;       // workspace word 0: zero before the first call, zero after each
-    int32_t* tile_counts;   // workspace [tiles, E]
-    int32_t* tile_rank;     // workspace [T, k]
+    uint8_t* tile_counts;   // workspace [tiles, E]
+    int32_t* tile_base;     // workspace [tiles, E]
+    uint8_t* tile_rank;     // workspace [T, k]
     int64_t max_rows;       // rows in out / out_scales / row_src
 };
 
-// Tokens per count tile (16, 32 or 64, growing with T) and the tile count.
+// Tokens per count tile (16, 32 or 64, growing with T; at most 64, so tile
+// counts and in-tile ranks fit a byte) and the tile count.
 int dispatch_tile_tokens(int64_t T);
 int64_t dispatch_tiles(int64_t T);
 
-// Workspace layout: [0, 256) control (the ticket counter in word 0), tile
-// counts [tiles, E] at counts_off, then (256-byte aligned) in-tile ranks
-// [T, k] at rank_off; total bytes.
+// Workspace layout (each part 256-byte aligned): byte tile counts
+// [tiles, E] at counts_off, tile prefixes int32 [tiles, E] at base_off, byte
+// in-tile ranks [T, k] at rank_off; total bytes. Nothing is kept between
+// calls.
 struct DispatchWorkspace {
     int tile_tokens;
     int64_t tiles;
-    size_t counts_off, rank_off, total;
+    size_t counts_off, base_off, rank_off, total;
 };
 DispatchWorkspace dispatch_workspace(int64_t T, int E, int k);
 
-// Up to three kernels: [route (only when routing falls back to its own
-// kernel)], count + scan, scatter. *n gets the number of kernels.
-hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream, LaunchInfo info[3], int* n,
+// Up to four kernels: [route (only when routing falls back to its own
+// kernel)], count (with routing inside when it applies), scan, scatter.
+// *n gets the number of kernels.
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream, LaunchInfo info[4], int* n,
                            bool run = true);
 
 hipError_t launch_combine(const void* expert_out, const int32_t* dst_row, const float* topk_w,

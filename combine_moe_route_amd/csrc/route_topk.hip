@@ -273,7 +273,7 @@ hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k, int n
                              float shared_w, int32_t* topk_idx, float* topk_w,
                              hipStream_t stream, LaunchInfo* info, bool run) {
     if (route_sort_applies(logits, E, k)) {
-        const int S = route_lanes(E);
+        const int S = route_lanes(T, E);
         const int64_t tokens_per_block = kRouteThreads / S;
         const int64_t blocks = (T + tokens_per_block - 1) / tokens_per_block;
         if (info) *info = LaunchInfo{blocks, kRouteThreads, 0, S};

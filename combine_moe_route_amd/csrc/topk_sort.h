@@ -50,10 +50,26 @@ __device__ __forceinline__ int cand_expert(double d) {
     return 1023 - (int)((uint32_t)__double2loint(d) & 1023u);
 }
 
+// Maximum and minimum of two packed candidates. The packed values are never
+// NaN (their exponent field is fixed), so the plain VALU instructions are
+// used directly: fmax / fmin would add a NaN-quieting pass over every operand
+// that the compiler cannot prove canonical (all of them, since they are built
+// from integer operations).
+__device__ __forceinline__ double dmax(double a, double b) {
+    double r;
+    asm("v_max_f64 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+__device__ __forceinline__ double dmin(double a, double b) {
+    double r;
+    asm("v_min_f64 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
 // a <- larger, b <- smaller
 __device__ __forceinline__ void cmpx(double& a, double& b) {
-    const double hi = fmax(a, b);
-    const double lo = fmin(a, b);
+    const double hi = dmax(a, b);
+    const double lo = dmin(a, b);
     a = hi;
     b = lo;
 }
@@ -79,7 +95,7 @@ __device__ __forceinline__ void sort_desc(double (&v)[K]) {
 template <int K>
 __device__ __forceinline__ void merge_top(double (&a)[K], const double (&b)[K]) {
 #pragma unroll
-    for (int i = 0; i < K; i++) a[i] = fmax(a[i], b[K - 1 - i]);
+    for (int i = 0; i < K; i++) a[i] = dmax(a[i], b[K - 1 - i]);
 #pragma unroll
     for (int j = K >> 1; j > 0; j >>= 1)
 #pragma unroll
@@ -195,11 +211,15 @@ __device__ __forceinline__ void write_route(const double (&list)[K], int g, int6
     }
 }
 
-// Lanes per token for a row of E logits: each lane holds at most
-// kRouteChunks chunks of 4.
-inline int route_lanes(int E) {
+// Lanes per token for T rows of E logits: each lane holds at most
+// kRouteChunks chunks of 4; beyond that, more lanes per token (shorter
+// per-lane work, one more merge round each doubling) while the grid has
+// fewer than about 2048 waves, so that small batches still spread over the
+// chip.
+inline int route_lanes(int64_t T, int E) {
     int S = 1;
     while (S < 16 && 4 * kRouteChunks * S < E) S <<= 1;
+    while (S < 16 && 4 * S < E && T * S < 2048 * 64) S <<= 1;
     return S;
 }
 

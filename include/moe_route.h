@@ -109,12 +109,10 @@ int moe_route_replicas(int32_t* topk_idx, int64_t T, int k, int E,
  * invalid or the count does not fit in int32. */
 int64_t moe_dispatch_max_rows(int64_t T, int E, int k, int row_align);
 
-/* Workspace bytes moe_dispatch and moe_route_dispatch need (a control word,
- * per-tile expert counts and in-tile ranks); 0 on invalid arguments.
- * The workspace must be zero-filled before its first use (e.g. once, right
- * after allocation); every completed call leaves its control word at zero
- * again, so a workspace can then be reused without clearing. The rest holds
- * nothing between calls. Calls sharing a workspace must not overlap. */
+/* Workspace bytes moe_dispatch and moe_route_dispatch need (per-tile expert
+ * counts and prefixes, in-tile ranks); 0 on invalid arguments. The
+ * workspace holds nothing between calls and needs no initialisation; calls
+ * sharing a workspace must not overlap. */
 size_t moe_dispatch_workspace_bytes(int64_t T, int E, int k, int groups);
 
 /*
@@ -158,12 +156,11 @@ size_t moe_dispatch_workspace_bytes(int64_t T, int E, int k, int groups);
  *   row_src        device int32 [max_rows] out: t*k+j of the pair in each
  *                  row, -1 for pad rows
  *   dst_row        device int32 [T, k] out: the row holding each pair
- *   workspace      device, >= moe_dispatch_workspace_bytes, 4-byte aligned,
- *                  zero-filled before its first use (see above)
+ *   workspace      device, >= moe_dispatch_workspace_bytes, 16-byte aligned
  * Rows at and beyond expert_offsets[E] are left untouched. max_rows is
  * moe_dispatch_max_rows(T, E, k, row_align). T == 0 writes zero counts and
- * offsets. Two kernels: counts, offsets and ranks in one launch, the rows in
- * a second.
+ * offsets. Three kernels: per-tile counts and ranks, the scan into offsets,
+ * the rows.
  */
 int moe_dispatch(const void* x, const int32_t* topk_idx,
                  int64_t T, int H, int E, int k, int groups, int row_align,
@@ -178,16 +175,15 @@ int moe_dispatch(const void* x, const int32_t* topk_idx,
  * mixture-of-experts communication", Introduction) feed the counts, offsets
  * and packing of "Enabling trillion-parameter models on AWS EFA", Dispatch
  * and Combine. When k <= 8, E <= 768, E % 4 == 0 and logits is 16-byte
- * aligned, routing runs inside the counting kernel (two launches in all);
- * otherwise moe_route_topk's kernel runs first (three launches).
+ * aligned, routing runs inside the counting kernel (three launches in all);
+ * otherwise moe_route_topk's kernel runs first (four launches).
  *
  *   logits         device fp32 [T, E], finite, 4-byte aligned
  *   topk_idx       device int32 [T, k] out (as moe_route_topk), then read by
  *                  the packing
  *   topk_w         device fp32 [T, k] out (as moe_route_topk)
- *   other arguments, limits and outputs as for moe_dispatch; the workspace
- *   (moe_dispatch_workspace_bytes) follows the same zero-before-first-use
- *   rule.
+ *   other arguments, limits and outputs as for moe_dispatch (workspace:
+ *   moe_dispatch_workspace_bytes).
  */
 int moe_route_dispatch(const float* logits, const void* x,
                        int64_t T, int H, int E, int k, int groups, int row_align,
@@ -211,10 +207,8 @@ int moe_route_dispatch(const float* logits, const void* x,
  *   MOE_EHIP if the scratch address cannot be obtained or a launch fails.
  * Every call on one GPU shares that GPU's array: calls that overlap on one
  * GPU (concurrent streams, or with a graph replay holding such a call) race
- * and give undefined results. Calls ordered on one stream are safe: the
- * array is zero when the library is loaded, each call rewrites what it reads
- * of it before reading it, and its control word returns to zero at the end
- * of every call.
+ * and give undefined results. Calls ordered on one stream are safe: each
+ * call writes what it reads of the array before reading it.
  */
 #define MOE_NO_ALLOC_SCRATCH_BYTES (16u << 20)
 

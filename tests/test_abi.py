@@ -57,13 +57,21 @@ def test_max_rows_and_workspace():
     assert lib.moe_dispatch_max_rows(10, 4, 2, 0) == -1          # row_align < 1
     assert lib.moe_dispatch_max_rows(10, 4, 2, 1025) == -1
     assert lib.moe_dispatch_max_rows(2 ** 28, 8, 8, 1) == -1     # rows overflow int32
-    # 256 bytes of control (the ticket counter), tile counts [tiles, E], then
-    # (256-byte aligned) in-tile ranks [T, k]; tiles of 16 tokens up to
-    # T = 1024, 32 up to 4096, else 64
-    assert lib.moe_dispatch_workspace_bytes(16384, 256, 8, 32) == 256 + 256 * 256 * 4 + 16384 * 8 * 4
-    assert lib.moe_dispatch_workspace_bytes(4096, 384, 8, 1) == 256 + 128 * 384 * 4 + 4096 * 8 * 4
-    assert lib.moe_dispatch_workspace_bytes(300, 8, 2, 1) == 1024 + 300 * 2 * 4   # 19 tiles
-    assert lib.moe_dispatch_workspace_bytes(0, 8, 2, 1) == 256
+    # each part 256-byte aligned: byte tile counts [tiles, E], int32 tile
+    # prefixes [tiles, E], byte in-tile ranks [T, k]; tiles of 16 tokens up
+    # to T = 1024, 32 up to 4096, else 64
+    def ws(T, E, k):
+        r = lambda n: (n + 255) // 256 * 256
+        tt = 16 if T <= 1024 else 32 if T <= 4096 else 64
+        tiles = (T + tt - 1) // tt
+        return r(tiles * ((E + 3) // 4 * 4)) + r(4 * tiles * E) + r(T * k)
+    assert lib.moe_dispatch_workspace_bytes(16384, 256, 8, 32) == 458752 == ws(16384, 256, 8)
+    assert lib.moe_dispatch_workspace_bytes(4096, 384, 8, 1) == 278528 == ws(4096, 384, 8)
+    assert lib.moe_dispatch_workspace_bytes(300, 8, 2, 1) == 1792 == ws(300, 8, 2)
+    assert lib.moe_dispatch_workspace_bytes(0, 8, 2, 1) == 0 == ws(0, 8, 2)
+    for T in (1, 16, 17, 1024, 1025, 4096, 4097, 100_000):
+        assert lib.moe_dispatch_workspace_bytes(T, 96, 6, 3) == ws(T, 96, 6)
+        assert lib.moe_dispatch_workspace_bytes(T, 65, 3, 5) == ws(T, 65, 3)   # rows padded to 68
     assert lib.moe_dispatch_workspace_bytes(300, 8, 2, 3) == 0   # E % groups != 0
 
 
@@ -180,9 +188,9 @@ def test_dispatch_no_alloc_validation():
     assert na(x=None) == ENULL
     assert na(out=A + 2 ** 20 + 4) == EALIGN
     # workspace needed beyond the static scratch
-    T_big = 600_000
-    assert lib.moe_dispatch_workspace_bytes(T_big, 8, 8, 1) > cap
-    assert na(T=T_big, E=8, k=8) == ENOSPC
+    T_big = 2_000_000
+    assert lib.moe_dispatch_workspace_bytes(T_big, 64, 8, 1) > cap
+    assert na(T=T_big, E=64, k=8) == ENOSPC
     assert lib.moe_dispatch_workspace_bytes(16384, 256, 8, 32) <= cap
 
 

@@ -4,10 +4,8 @@ CPU oracle and against moe_route_topk followed by moe_dispatch.
 
 Routing, counts, offsets, group offsets, both row maps, rows and FP8 scales
 must be bit-exact; router weights within 1e-5 relative of the oracle and
-bitwise equal to moe_route_topk's. The counting kernel's last block scans
-after a ticket that must return to zero after every call: reuse of one
-workspace across calls of different sizes and across both entry points is
-checked too."""
+bitwise equal to moe_route_topk's. Reuse of one workspace across calls of
+different sizes and across both entry points is checked too."""
 import numpy as np
 import pytest
 import torch
@@ -66,8 +64,6 @@ def fused_case(T, H, E, k, groups=1, row_align=1, fp8=False, seed=0, zipf_s=None
     assert np.array_equal(g["out"], ref.out), "payload"
     if fp8:
         assert np.array_equal(g["scales"], ref.scales.view(np.uint32)), "scales"
-    # the control word is back at zero
-    assert int(b.workspace[:4].view(torch.int32).item()) == 0, "ticket not reset"
     if check_two_call:
         i2, w2 = moe_route_topk(logits, k)
         b2 = moe_dispatch(x, i2, E, groups, row_align, fp8)
@@ -138,7 +134,7 @@ def test_fused_ties_and_signed_zero(dev):
 def test_one_workspace_across_calls_and_sizes(dev):
     """One workspace (and one set of buffers, sized for the largest call)
     serves calls of different sizes and both entry points in a row; every
-    result matches the oracle and the ticket is zero after each call."""
+    result matches the oracle."""
     from combine_moe_route_amd import DispatchBuffers, alloc_dispatch, moe_dispatch
     E, k, H, G, A = 256, 8, 256, 32, 128
     big = alloc_dispatch(4096, H, E, k, G, A, True, dev)
@@ -157,7 +153,6 @@ def test_one_workspace_across_calls_and_sizes(dev):
             moe_dispatch(x, idx, E, G, A, True, view(0))
             torch.cuda.synchronize()
             assert big.expert_offsets.cpu().tolist() == [0] * (E + 1)
-            assert int(big.workspace[:4].view(torch.int32).item()) == 0
             continue
         if i % 2 == 0:
             fused_case(T, H, E, k, G, A, True, seed=i, dev=dev, bufs=view(T), check_two_call=False)
@@ -171,7 +166,6 @@ def test_one_workspace_across_calls_and_sizes(dev):
             assert np.array_equal(b.expert_offsets.cpu().numpy(), ref.expert_offsets)
             assert np.array_equal(b.dst_row.cpu().numpy(), ref.dst_row)
             assert np.array_equal(b.out[:ref.num_rows].cpu().numpy(), ref.out)
-            assert int(b.workspace[:4].view(torch.int32).item()) == 0
 
 
 def test_fused_repeat_bit_identical(dev):

@@ -57,7 +57,7 @@ def test_no_alloc_rejects_oversize_without_launch():
     from combine_moe_route_amd import MoeRouteError, alloc_dispatch, moe_dispatch_no_alloc
     from combine_moe_route_amd.binding import MOE_ENOSPC
     dev = torch.device("cuda:0")
-    T, H, E, k = 600_000, 8, 8, 8
+    T, H, E, k = 2_000_000, 8, 64, 8
     x = torch.zeros((T, H), dtype=torch.bfloat16, device=dev)
     idx = torch.zeros((T, k), dtype=torch.int32, device=dev)
     bufs = alloc_dispatch(T, H, E, k, 1, 1, False, dev, workspace=False)
