@@ -181,12 +181,7 @@ int dispatch_impl(const float* logits, float* topk_w, const void* x, const int32
 
     const hipError_t e = moe::launch_dispatch(a, stream, info, &nk);
     if (log_enabled())
-        for (int i = 0; i < nk; i++)
-            log_launch(i == nk - 1   ? "dispatch.scatter"
-                       : i == nk - 2 ? "dispatch.scan"
-                       : i == nk - 3 ? (route && nk == 3 ? "dispatch.route_count" : "dispatch.count")
-                                     : "dispatch.route",
-                       info[i]);
+        for (int i = 0; i < nk; i++) log_launch(info[i].name ? info[i].name : "dispatch", info[i]);
     return status_of(e);
 }
 

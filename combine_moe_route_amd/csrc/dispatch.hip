@@ -31,6 +31,10 @@
 //           and stores it to its k rows (FP8: one quantisation per token, k
 //           stores); the chunk-0 wave publishes dst_row / row_src. Leading
 //           blocks zero the pad rows.
+// Small batches (at most 64 tiles and 4096 tile counts, e.g. 128-token decode)
+// skip the scan launch: every scatter block stages the byte counts itself and
+// builds the tile prefixes and offsets in LDS while its x row is in flight
+// (block 0 writes the count and offset outputs).
 #include "moe_device.h"
 #include "launch.h"
 #include "topk_sort.h"
@@ -360,6 +364,75 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(const uint8_t* __restrict
 
 // ---------------------------------------------------------------- scatter
 
+// Inline scan for small batches: tiles <= kInlineTiles and tiles * E <=
+// kInlineCells. Every thread of the block takes part (it holds barriers).
+constexpr int kInlineTiles = 64;
+constexpr int kInlineCells = 4096;
+
+struct InlineLds {
+    int32_t tb[kInlineCells];        // tile prefixes [tiles, E]
+    int32_t off[kMaxExperts + 1];    // segment offsets
+    int32_t tot[kMaxExperts];        // expert totals
+    int32_t wave[1024 / kWave];
+};
+
+__device__ void inline_scan(const uint8_t* __restrict__ counts, int tiles, int E, int row_align,
+                            int groups, bool write_out, int32_t* __restrict__ g_counts,
+                            int32_t* __restrict__ g_offsets, int32_t* __restrict__ g_goffs,
+                            InlineLds& L) {
+    const int NT = blockDim.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int E4 = (E + 3) & ~3;
+    for (int i = tid; i < tiles * E; i += NT) {
+        const int b = i / E;
+        L.tb[i] = counts[b * E4 + (i - b * E)];
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += NT) {
+        int run = 0;
+        for (int b = 0; b < tiles; b++) {
+            const int c = L.tb[b * E + e];
+            L.tb[b * E + e] = run;
+            run += c;
+        }
+        L.tot[e] = run;
+    }
+    __syncthreads();
+    // exclusive scan of the padded totals over experts: thread tid owns the
+    // contiguous experts [e0, e1)
+    const int per = (E + NT - 1) / NT;
+    const int e0 = min(E, tid * per);
+    const int e1 = min(E, e0 + per);
+    int local = 0;
+    for (int e = e0; e < e1; e++) local += (L.tot[e] + row_align - 1) / row_align * row_align;
+    const int incl = wave_inclusive_sum(local);
+    if (lane == kWave - 1) L.wave[wave] = incl;
+    __syncthreads();
+    if (wave == 0) {
+        const int v = lane < NT / kWave ? L.wave[lane] : 0;
+        const int vi = wave_inclusive_sum(v);
+        if (lane < NT / kWave) L.wave[lane] = vi - v;
+    }
+    __syncthreads();
+    int run = L.wave[wave] + incl - local;
+    for (int e = e0; e < e1; e++) {
+        L.off[e] = run;
+        run += (L.tot[e] + row_align - 1) / row_align * row_align;
+        if (e == E - 1) L.off[E] = run;
+    }
+    __syncthreads();
+    if (write_out) {
+        for (int e = tid; e <= E; e += NT) {
+            g_offsets[e] = L.off[e];
+            if (e < E) g_counts[e] = L.tot[e];
+        }
+        if (g_goffs != nullptr)
+            for (int gi = tid; gi <= groups; gi += NT) g_goffs[gi] = L.off[gi * (E / groups)];
+    }
+}
+
 constexpr int kScatterThreads = 256;
 
 // Zero the pad rows of one expert's segment, or the part of them this
@@ -435,34 +508,54 @@ __device__ __forceinline__ void publish_rows(int lane, int64_t p0, int j0, int k
 // and tile bases come in through scalar loads; the x row is read once through
 // a range descriptor (lanes past the row read zeros) and stored to each of the
 // token's rows.
+// Scan outputs as the scatter reads them: offsets [E+1], counts [E] and tile
+// prefixes [tiles, E], from global memory (scan kernel) or from LDS (inline).
+struct ScanView {
+    const int32_t* off;
+    const int32_t* cnt;
+    const int32_t* tb;
+};
+
+template <bool INLINE>
 __global__ __launch_bounds__(kScatterThreads) void k_scatter_bf16(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ topk_idx,
     const uint8_t* __restrict__ tile_rank, const int32_t* __restrict__ tile_base,
-    const int32_t* __restrict__ expert_counts, const int32_t* __restrict__ expert_offsets,
+    const uint8_t* __restrict__ tile_counts, int tiles, int row_align, int groups,
+    int32_t* __restrict__ group_offsets,
+    int32_t* __restrict__ expert_counts, int32_t* __restrict__ expert_offsets,
     int64_t T, int H, int E, int k, int TT, int64_t max_rows, int pad_blocks,
     int pad_blocks_per_expert, int pad_rows_per_block, unsigned char* __restrict__ out,
     int32_t* __restrict__ row_src, int32_t* __restrict__ dst_row) {
-    if ((int)blockIdx.x < pad_blocks) {
-        zero_pad_rows(blockIdx.x, pad_blocks_per_expert, pad_rows_per_block, H, false, max_rows,
-                      expert_counts, expert_offsets, out, nullptr, row_src);
-        return;
-    }
     const int lane = threadIdx.x & (kWave - 1);
     const int U = H / 8;                           // 16-byte units per row
     const int CW = (U + kWave - 1) / kWave;        // waves per token
+    const bool pad_block = (int)blockIdx.x < pad_blocks;
     const int64_t gw = (int64_t)(blockIdx.x - pad_blocks) * kScatterWaves +
                        __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int64_t t = gw / CW;
-    if (t >= T) return;
+    const int64_t t = pad_block ? T : gw / CW;
     const int chunk = (int)(gw - t * CW);
     const int u = chunk * kWave + lane;
-
-    const uint4 a = load16_nt(range_rsrc(x + t * (int64_t)H, 2 * H), 16 * u);
+    // the x row first, so that its load overlaps the inline scan
+    uint4 a = make_uint4(0u, 0u, 0u, 0u);
+    if (t < T) a = load16_nt(range_rsrc(x + t * (int64_t)H, 2 * H), 16 * u);
+    ScanView sv{expert_offsets, expert_counts, tile_base};
+    if constexpr (INLINE) {
+        __shared__ InlineLds L;
+        inline_scan(tile_counts, tiles, E, row_align, groups, blockIdx.x == 0, expert_counts,
+                    expert_offsets, group_offsets, L);
+        sv = ScanView{L.off, L.tot, L.tb};
+    }
+    if (pad_block) {
+        zero_pad_rows(blockIdx.x, pad_blocks_per_expert, pad_rows_per_block, H, false, max_rows,
+                      sv.cnt, sv.off, out, nullptr, row_src);
+        return;
+    }
+    if (t >= T) return;
     const int64_t p0 = t * k;
-    const int32_t* tb = tile_base + (t / TT) * E;
+    const int32_t* tb = sv.tb + (t / TT) * E;
     for (int j0 = 0; j0 < k; j0 += 8) {
         int r[8];
-        slot_rows(topk_idx, tile_rank, expert_offsets, tb, p0, j0, k, E, max_rows, r);
+        slot_rows(topk_idx, tile_rank, sv.off, tb, p0, j0, k, E, max_rows, r);
         if (chunk == 0) publish_rows(lane, p0, j0, k, r, dst_row, row_src);
         if (u < U) {
 #pragma unroll
@@ -480,34 +573,52 @@ __global__ __launch_bounds__(kScatterThreads) void k_scatter_bf16(
 // to each destination row, and its 1x128 scales are staged in LDS and written
 // to each row's scale segment with one contiguous store (instead of many small
 // pieces from different waves, which cost HBM read-modify-write cycles).
+template <bool INLINE>
 __global__ __launch_bounds__(1024) void k_scatter_fp8(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ topk_idx,
     const uint8_t* __restrict__ tile_rank, const int32_t* __restrict__ tile_base,
-    const int32_t* __restrict__ expert_counts, const int32_t* __restrict__ expert_offsets,
+    const uint8_t* __restrict__ tile_counts, int tiles, int row_align, int groups,
+    int32_t* __restrict__ group_offsets,
+    int32_t* __restrict__ expert_counts, int32_t* __restrict__ expert_offsets,
     int64_t T, int H, int E, int k, int TT, int64_t max_rows, int pad_blocks,
     int pad_blocks_per_expert, int pad_rows_per_block, unsigned char* __restrict__ out,
     float* __restrict__ scales, int32_t* __restrict__ row_src, int32_t* __restrict__ dst_row) {
     extern __shared__ float s_scale[];             // [H / 128]
-    if ((int)blockIdx.x < pad_blocks) {
-        zero_pad_rows(blockIdx.x, pad_blocks_per_expert, pad_rows_per_block, H, true, max_rows,
-                      expert_counts, expert_offsets, out, scales, row_src);
-        return;
-    }
-    const int64_t t = blockIdx.x - pad_blocks;
+    const bool pad_block = (int)blockIdx.x < pad_blocks;
+    const int64_t t = pad_block ? 0 : blockIdx.x - pad_blocks;
     const int lane = threadIdx.x & (kWave - 1);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int W = blockDim.x / kWave;
     const int U = H / 16;                          // lane units per row
     const int CW = (U + kWave - 1) / kWave;
     const int nb = H / 128;
-    const auto xr = range_rsrc(x + t * (int64_t)H, 2 * H);
+    const auto xr = range_rsrc(x + t * (int64_t)H, pad_block ? 0 : 2 * H);
+    // the first chunk of the x row first, so that its load overlaps the
+    // inline scan
+    uint4 a0 = make_uint4(0u, 0u, 0u, 0u), b0 = a0;
+    if (!pad_block && w < CW) {
+        a0 = load16_nt(xr, 32 * (w * kWave + lane));
+        b0 = load16_nt(xr, 32 * (w * kWave + lane) + 16);
+    }
+    ScanView sv{expert_offsets, expert_counts, tile_base};
+    if constexpr (INLINE) {
+        __shared__ InlineLds L;
+        inline_scan(tile_counts, tiles, E, row_align, groups, blockIdx.x == 0, expert_counts,
+                    expert_offsets, group_offsets, L);
+        sv = ScanView{L.off, L.tot, L.tb};
+    }
+    if (pad_block) {
+        zero_pad_rows(blockIdx.x, pad_blocks_per_expert, pad_rows_per_block, H, true, max_rows,
+                      sv.cnt, sv.off, out, scales, row_src);
+        return;
+    }
     const int64_t p0 = t * k;
-    const int32_t* tb = tile_base + (t / TT) * E;
+    const int32_t* tb = sv.tb + (t / TT) * E;
 
     for (int chunk = w; chunk < CW; chunk += W) {
         const int u = chunk * kWave + lane;
-        const uint4 a = load16_nt(xr, 32 * u);
-        const uint4 b = load16_nt(xr, 32 * u + 16);
+        const uint4 a = chunk == w ? a0 : load16_nt(xr, 32 * u);
+        const uint4 b = chunk == w ? b0 : load16_nt(xr, 32 * u + 16);
         float f[16];
         unpack8(a, f);
         unpack8(b, f + 8);
@@ -526,7 +637,7 @@ __global__ __launch_bounds__(1024) void k_scatter_fp8(
         if (u < U && (u & 7) == 0) s_scale[u >> 3] = s;
         for (int j0 = 0; j0 < k; j0 += 8) {
             int r[8];
-            slot_rows(topk_idx, tile_rank, expert_offsets, tb, p0, j0, k, E, max_rows, r);
+            slot_rows(topk_idx, tile_rank, sv.off, tb, p0, j0, k, E, max_rows, r);
             if (chunk == 0) publish_rows(lane, p0, j0, k, r, dst_row, row_src);
             if (u < U) {
 #pragma unroll
@@ -541,7 +652,7 @@ __global__ __launch_bounds__(1024) void k_scatter_fp8(
     for (int j = w; j < k; j += W) {
         const int e = topk_idx[p0 + j];
         if ((unsigned)e >= (unsigned)E) continue;
-        const int rr = expert_offsets[e] + tb[e] + tile_rank[p0 + j];
+        const int rr = sv.off[e] + tb[e] + tile_rank[p0 + j];
         if (rr < 0 || rr >= max_rows) continue;
         for (int i = lane; i < nb; i += kWave) scales[(int64_t)rr * nb + i] = s_scale[i];
     }
@@ -582,6 +693,8 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream, LaunchInfo
     const size_t count_lds = (size_t)a.E * sizeof(uint64_t) +
                              (fused ? (size_t)TT * a.k * sizeof(int32_t) : 0);
     const int64_t scan_blocks = tiles < 1 ? 1 : tiles < kScanBlocks ? tiles : kScanBlocks;
+    // small batches scan inside the scatter (there must be scatter blocks)
+    const bool inline_scan_ok = a.T > 0 && tiles <= kInlineTiles && tiles * a.E <= kInlineCells;
 
     int pad_per_expert = 0, pad_rows_per_block = 0;
     if (a.row_align > 1 && a.T > 0) {
@@ -603,14 +716,18 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream, LaunchInfo
         (void)launch_route_topk(a.logits, a.T, a.E, a.k, 0, 0.0f, const_cast<int32_t*>(a.topk_idx),
                                 a.topk_w, stream, &route_info, false);
     if (info) {
-        if (route_first) info[nk++] = route_info;
-        info[nk++] = LaunchInfo{tiles, count_threads, count_lds, fused ? S : TT};
-        info[nk++] = LaunchInfo{scan_blocks, kScanThreads, 0, tiles};
+        if (route_first) info[nk++] = LaunchInfo{route_info.grid, route_info.block, route_info.lds,
+                                                 route_info.param, "route"};
+        info[nk++] = LaunchInfo{tiles, count_threads, count_lds, fused ? S : TT,
+                                fused ? "route_count" : "count"};
+        if (!inline_scan_ok) info[nk++] = LaunchInfo{scan_blocks, kScanThreads, 0, tiles, "scan"};
         info[nk++] = a.fp8 ? LaunchInfo{scatter_blocks, fp8_threads,
-                                        (size_t)(a.H / 128) * sizeof(float), fp8_waves}
-                           : LaunchInfo{scatter_blocks, kScatterThreads, 0, bf16_waves_per_token};
+                                        (size_t)(a.H / 128) * sizeof(float), fp8_waves,
+                                        inline_scan_ok ? "scan+scatter" : "scatter"}
+                           : LaunchInfo{scatter_blocks, kScatterThreads, 0, bf16_waves_per_token,
+                                        inline_scan_ok ? "scan+scatter" : "scatter"};
     } else {
-        nk = route_first ? 4 : 3;
+        nk = (route_first ? 1 : 0) + (inline_scan_ok ? 2 : 3);
     }
     if (n) *n = nk;
     if (!run) return hipSuccess;
@@ -634,10 +751,12 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream, LaunchInfo
         }
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
-    k_scan<<<dim3((unsigned)scan_blocks), kScanThreads, 0, stream>>>(
-        a.tile_counts, tiles, a.E, a.row_align, a.groups, a.tile_base, a.expert_counts,
-        a.expert_offsets, a.group_offsets);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (!inline_scan_ok) {
+        k_scan<<<dim3((unsigned)scan_blocks), kScanThreads, 0, stream>>>(
+            a.tile_counts, tiles, a.E, a.row_align, a.groups, a.tile_base, a.expert_counts,
+            a.expert_offsets, a.group_offsets);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
 
     // scatter: leading blocks zero pad rows, then the token work
     unsigned char* out = static_cast<unsigned char*>(a.out);
@@ -645,15 +764,19 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream, LaunchInfo
     if (scatter_blocks == 0) return hipSuccess;
     if (a.fp8) {
         const size_t lds = (size_t)(a.H / 128) * sizeof(float);
-        k_scatter_fp8<<<dim3((unsigned)scatter_blocks), dim3(fp8_threads), lds, stream>>>(
-            x, a.topk_idx, a.tile_rank, a.tile_base, a.expert_counts, a.expert_offsets, a.T, a.H,
-            a.E, a.k, TT, a.max_rows, (int)pad_blocks, pad_per_expert, pad_rows_per_block, out,
-            a.out_scales, a.row_src, a.dst_row);
-    } else {
-        k_scatter_bf16<<<dim3((unsigned)scatter_blocks), dim3(kScatterThreads), 0, stream>>>(
-            x, a.topk_idx, a.tile_rank, a.tile_base, a.expert_counts, a.expert_offsets, a.T, a.H,
-            a.E, a.k, TT, a.max_rows, (int)pad_blocks, pad_per_expert, pad_rows_per_block, out,
+        auto kern = inline_scan_ok ? k_scatter_fp8<true> : k_scatter_fp8<false>;
+        kern<<<dim3((unsigned)scatter_blocks), dim3(fp8_threads), lds, stream>>>(
+            x, a.topk_idx, a.tile_rank, a.tile_base, a.tile_counts, (int)tiles, a.row_align,
+            a.groups, a.group_offsets, a.expert_counts, a.expert_offsets, a.T, a.H, a.E, a.k, TT,
+            a.max_rows, (int)pad_blocks, pad_per_expert, pad_rows_per_block, out, a.out_scales,
             a.row_src, a.dst_row);
+    } else {
+        auto kern = inline_scan_ok ? k_scatter_bf16<true> : k_scatter_bf16<false>;
+        kern<<<dim3((unsigned)scatter_blocks), dim3(kScatterThreads), 0, stream>>>(
+            x, a.topk_idx, a.tile_rank, a.tile_base, a.tile_counts, (int)tiles, a.row_align,
+            a.groups, a.group_offsets, a.expert_counts, a.expert_offsets, a.T, a.H, a.E, a.k, TT,
+            a.max_rows, (int)pad_blocks, pad_per_expert, pad_rows_per_block, out, a.row_src,
+            a.dst_row);
     }
     return hipGetLastError();
 }

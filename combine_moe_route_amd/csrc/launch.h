@@ -15,7 +15,8 @@ struct LaunchInfo {
     int64_t grid = 0;
     int block = 0;
     size_t lds = 0;
-    int64_t param = 0;   // kernel-specific: lanes per token, tokens per block, ...
+    int64_t param = 0;           // kernel-specific: lanes per token, tokens per block, ...
+    const char* name = nullptr;  // for the launch log
 };
 
 // A launch packet counts work-items in 32 bits (grid_size_x) and blocks in
@@ -74,8 +75,8 @@ struct DispatchWorkspace {
 DispatchWorkspace dispatch_workspace(int64_t T, int E, int k);
 
 // Up to four kernels: [route (only when routing falls back to its own
-// kernel)], count (with routing inside when it applies), scan, scatter.
-// *n gets the number of kernels.
+// kernel)], count (with routing inside when it applies), [scan (small
+// batches scan inside the scatter)], scatter. *n gets the number of kernels.
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream, LaunchInfo info[4], int* n,
                            bool run = true);
 
