@@ -181,8 +181,9 @@ __device__ __forceinline__ int wave_inclusive_sum(int v) {
 
 // Up to kScanBlocks blocks of 1024 threads. Thread tid = p * Qp + q handles
 // the four experts 4q .. 4q+3 (Q = ceil(E / 4) groups, Qp = Q rounded up to a
-// power of two), P = min(1024 / Qp, 16) threads sharing a group (the rest
-// only take part in the expert scan). Every block reads all
+// power of two), P = min(1024 / Qp, 4) threads sharing a group (the rest
+// only take part in the expert scan; more sharers would cost more in the
+// exchange of partial sums than they save in the column sums). Every block reads all
 // byte counts (into LDS, in chunks of 64 KiB) and computes every expert's
 // total and, for its own range of tiles, every expert's prefix at the range
 // start; every block then scans the padded totals over experts (the same
@@ -190,7 +191,7 @@ __device__ __forceinline__ int wave_inclusive_sum(int v) {
 // prefixes (relative to the segment start) of its own range only, so the
 // stores spread over the blocks and no block waits for another.
 constexpr int kScanBlocks = 32;
-constexpr int kScanShare = 16;   // at most this many threads per expert group
+constexpr int kScanShare = 4;   // at most this many threads per expert group
 
 __global__ __launch_bounds__(kScanThreads) void k_scan(const uint8_t* __restrict__ tile_counts,
                                                        int64_t tiles, int E, int row_align,
@@ -275,12 +276,14 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(const uint8_t* __restrict
     __syncthreads();
     int cnt[4] = {0, 0, 0, 0}, start[4] = {0, 0, 0, 0};
     if (real)
-        for (int pp = 0; pp < P; pp++)
 #pragma unroll
-            for (int b = 0; b < 4; b++) {
-                cnt[b] += s_all[b][pp * Qp + q];
-                start[b] += s_pre[b][pp * Qp + q];
-            }
+        for (int pp = 0; pp < kScanShare; pp++)
+            if (pp < P)
+#pragma unroll
+                for (int b = 0; b < 4; b++) {
+                    cnt[b] += s_all[b][pp * Qp + q];
+                    start[b] += s_pre[b][pp * Qp + q];
+                }
     int padded[4];
 #pragma unroll
     for (int b = 0; b < 4; b++)
