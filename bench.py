@@ -455,6 +455,9 @@ def cu_budget(w, steps, co="bf16"):
     moe_route_topk(logits, w.k, idx, wt)
     moe_dispatch(x, idx, w.E, w.groups, w.row_align, w.fp8, bufs)
     moe_harness_expert_scale(bufs, idx, w.E, w.fp8, expert_out=eo)
+    torch.cuda.synchronize()
+    bytes_step = sum(algorithmic_bytes(w.T, w.H, w.E, w.k, int(bufs.expert_offsets[-1].item()),
+                                       w.fp8))
     gen = torch.Generator(device=dev).manual_seed(0)
     if co == "grouped":
         from combine_moe_route_amd import moe_grouped_gemm_fp8, moe_grouped_gemm_workspace_bytes
@@ -522,6 +525,13 @@ def cu_budget(w, steps, co="bf16"):
             s_moe = masked(cus)
             t_moe = timed(moe_step, steps, s_moe)
         row = dict(cus=n if n else "all (shared)", us_moe_step=round(t_moe, 1))
+        if n:
+            # the budget's own ceiling: a 1 GiB device copy on the same CUs
+            with torch.cuda.stream(s_moe):
+                cpy = copy_bandwidth()
+            row.update(copy_GBps_on_budget=round(cpy, 1),
+                       us_moe_step_at_copy_rate=round(
+                           (bytes_step / (cpy * 1e9)) * 1e6, 1))
         if rest:
             if n:
                 s_rest = masked(rest)
@@ -559,13 +569,14 @@ def cu_budget(w, steps, co="bf16"):
 
 
 def copy_bandwidth(nbytes=1 << 30, reps=10):
-    """Device-to-device copy bandwidth (read + write bytes / time)."""
+    """Device-to-device copy bandwidth (read + write bytes / time) on torch's
+    current stream."""
     import torch
     a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
     a.fill_(3)
     b.copy_(a)
-    torch.cuda.synchronize()
+    torch.cuda.current_stream().synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
