@@ -3,10 +3,15 @@
 Only the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
 leg may import this package. The HIP library and its binding never do.
 
-The arithmetic lives in ``moe_oracle.c`` (plain single-threaded C, fp64 where
-the method leaves the precision open). This module builds it with gcc and
-wraps its functions for numpy arrays. bf16 arrays are uint16 bit patterns,
-E4M3 arrays are uint8 codes.
+The arithmetic lives in ``moe_oracle.c`` (plain C, fp64 where the method
+leaves the precision open). ``build()`` compiles it with gcc three times:
+``plain`` (single-threaded, the default), ``omp`` (the same source with
+-fopenmp: its pragmas spread independent per-token and per-block iterations
+over the host cores) and ``san`` (single-threaded, with AddressSanitizer and
+UndefinedBehaviorSanitizer; load it in a process started with libasan
+preloaded). Loading never compiles: a missing or stale library raises, so a
+benchmark never builds anything on the machine it measures. bf16 arrays are
+uint16 bit patterns, E4M3 arrays are uint8 codes.
 """
 from __future__ import annotations
 
@@ -19,28 +24,58 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.c")
-_LIB = os.path.join(_HERE, "libmoeoracle.so")
 
-GCC_CMD = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
-           "-fno-fast-math", "-Wall", "-Wextra", "-o", _LIB, _SRC, "-lm"]
+_COMMON = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
+           "-Wall", "-Wextra"]
+VARIANTS = {
+    "plain": (os.path.join(_HERE, "libmoeoracle.so"), ["-Wno-unknown-pragmas"]),
+    "omp": (os.path.join(_HERE, "libmoeoracle_omp.so"), ["-fopenmp"]),
+    "san": (os.path.join(_HERE, "libmoeoracle_san.so"),
+            ["-Wno-unknown-pragmas", "-g", "-fno-omit-frame-pointer",
+             "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined"]),
+}
 
 
-def build() -> str:
-    """Compile the oracle with gcc; returns the library path."""
-    subprocess.run(GCC_CMD, check=True)
-    return _LIB
+def gcc_command(variant: str):
+    path, extra = VARIANTS[variant]
+    return _COMMON + extra + ["-o", path, _SRC, "-lm"]
 
 
-_lib = None
+def build(variants=tuple(VARIANTS)) -> None:
+    """Compile the oracle library variants with gcc."""
+    for v in variants:
+        subprocess.run(gcc_command(v), check=True)
+
+
+def stale(variant: str) -> bool:
+    path = VARIANTS[variant][0]
+    return not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC)
+
+
+_variant = os.environ.get("MOE_ORACLE_VARIANT", "plain")
+_libs = {}
+
+
+def set_variant(variant: str) -> None:
+    """Library variant used by the calls that follow (plain, omp or san)."""
+    global _variant
+    if variant not in VARIANTS:
+        raise ValueError(f"unknown oracle variant {variant!r}")
+    _variant = variant
+
+
+def variant() -> str:
+    return _variant
 
 
 def _load():
-    global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        build()
-    lib = ctypes.CDLL(_LIB)
+    if _variant in _libs:
+        return _libs[_variant]
+    path = VARIANTS[_variant][0]
+    if stale(_variant):
+        raise RuntimeError(f"oracle library {path} is missing or older than {_SRC}; "
+                           "build it first (python -c 'import oracle; oracle.build()')")
+    lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     i64, i32 = ctypes.c_int64, ctypes.c_int
     lib.oracle_route_topk.argtypes = [P, i64, i32, i32, P, P]
@@ -60,6 +95,8 @@ def _load():
     lib.oracle_bf16_from_double.restype = ctypes.c_uint16
     lib.oracle_quantize_block.argtypes = [P, P, P]
     lib.oracle_quantize_block.restype = None
+    lib.oracle_quantize_blocks.argtypes = [P, i64, P, P]
+    lib.oracle_quantize_blocks.restype = None
     lib.oracle_combine_sender.argtypes = [P, P, P, P, i64, i32, i32, i32, i32, P, P, P]
     lib.oracle_combine_sender.restype = None
     lib.oracle_route_topk_shared.argtypes = [P, i64, i32, i32, i32, ctypes.c_float, P, P]
@@ -76,7 +113,7 @@ def _load():
     lib.oracle_grouped_gemm_fp8.restype = None
     lib.oracle_grouped_gemm_fp8_at.argtypes = [P, P, P, i32, P, P, i32, i32, P, P, i64, P, P, P]
     lib.oracle_grouped_gemm_fp8_at.restype = None
-    _lib = lib
+    _libs[_variant] = lib
     return lib
 
 
@@ -237,6 +274,18 @@ def quantize_block(xblock: np.ndarray):
     s = np.empty(1, np.float32)
     _load().oracle_quantize_block(_p(xb), _p(q), _p(s))
     return q, s[0]
+
+
+def quantize_blocks(x: np.ndarray):
+    """(codes uint8 [n, 128], scales float32 [n]) for n 1x128 bf16 blocks
+    [n, 128] (uint16)."""
+    xb = _c(x, np.uint16)
+    assert xb.ndim == 2 and xb.shape[1] == 128
+    n = xb.shape[0]
+    q = np.empty((n, 128), np.uint8)
+    s = np.empty(n, np.float32)
+    _load().oracle_quantize_blocks(_p(xb), n, _p(q), _p(s))
+    return q, s
 
 
 def quantize_weights(w: np.ndarray):

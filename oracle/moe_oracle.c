@@ -1,11 +1,14 @@
 /*
  * CPU oracle for the MoE token dispatch / combine path.
  *
- * TEST INFRASTRUCTURE ONLY. Plain, slow, single-threaded C that states what
- * the path computes. Only the tests, the smoke check and the benchmark's CPU
- * baseline use it; the HIP library never links, includes or calls it, and
- * the two share no source. Build: gcc -O2 -std=c11 -fPIC -shared (no
- * fast-math, SSE arithmetic, default round-to-nearest-even mode).
+ * TEST INFRASTRUCTURE ONLY. Plain, slow C that states what the path
+ * computes. Only the tests, the smoke check and the benchmark's CPU baseline
+ * use it; the HIP library never links, includes or calls it, and the two
+ * share no source. Build: gcc -O2 -std=c11 -fPIC -shared (no fast-math, SSE
+ * arithmetic, default round-to-nearest-even mode), single-threaded. The same
+ * source is also built with -fopenmp: the only pragmas spread independent
+ * per-token (or per-block) iterations over threads; counting, offsets and the
+ * stable placement stay serial, and no arithmetic changes.
  *
  * Sources (Perplexity engineering posts):
  *  [EPMC] "Efficient and portable mixture-of-experts communication",
@@ -131,8 +134,11 @@ void oracle_quantize_block(const uint16_t* x, uint8_t* q, float* s_out) {
  * create. Slot j holds the j-th best expert. */
 void oracle_route_topk(const float* logits, int64_t T, int E, int k,
                        int32_t* topk_idx, float* topk_w) {
+#pragma omp parallel
+    {
     double* p = (double*)malloc(sizeof(double) * (size_t)E);
     unsigned char* taken = (unsigned char*)malloc((size_t)E);
+#pragma omp for schedule(static)
     for (int64_t t = 0; t < T; t++) {
         const float* l = logits + t * (int64_t)E;
         /* softmax over all experts, in fp64 */
@@ -160,6 +166,7 @@ void oracle_route_topk(const float* logits, int64_t T, int E, int k,
     }
     free(p);
     free(taken);
+    }
 }
 
 /* ---------------------------------------------------------------- dispatch */
@@ -221,8 +228,11 @@ int64_t oracle_dispatch(const uint16_t* x, const int32_t* topk_idx,
     }
     /* payload */
     const int nb = H / 128;
+#pragma omp parallel
+    {
     uint8_t* qrow = fp8 ? (uint8_t*)malloc((size_t)H) : NULL;
     float* srow = fp8 ? (float*)malloc(sizeof(float) * (size_t)(nb > 0 ? nb : 1)) : NULL;
+#pragma omp for schedule(static)
     for (int64_t t = 0; t < T; t++) {
         const uint16_t* xr = x + t * (int64_t)H;
         if (fp8)
@@ -239,6 +249,9 @@ int64_t oracle_dispatch(const uint16_t* x, const int32_t* topk_idx,
             }
         }
     }
+    free(qrow);
+    free(srow);
+    }
     /* pad rows: zero payload and zero scales */
     for (int e = 0; e < E; e++)
         for (int64_t r = expert_offsets[e] + expert_counts[e]; r < expert_offsets[e + 1]; r++) {
@@ -249,8 +262,6 @@ int64_t oracle_dispatch(const uint16_t* x, const int32_t* topk_idx,
                 memset((uint16_t*)out + r * H, 0, sizeof(uint16_t) * (size_t)H);
             }
         }
-    free(qrow);
-    free(srow);
     return expert_offsets[E];
 }
 
@@ -290,6 +301,7 @@ void oracle_expert_scale(const void* disp, const float* scales,
  * slot order, rounded once to bf16. Dropped slots (dst_row < 0) add nothing. */
 void oracle_combine(const uint16_t* expert_out, const int32_t* dst_row,
                     const float* topk_w, int64_t T, int H, int k, uint16_t* y) {
+#pragma omp parallel for schedule(static)
     for (int64_t t = 0; t < T; t++)
         for (int h = 0; h < H; h++) {
             double acc = 0.0;
@@ -303,6 +315,13 @@ void oracle_combine(const uint16_t* expert_out, const int32_t* dst_row,
 }
 
 /* ---------------------------------------------------------------- helpers */
+
+/* Many 1x128 blocks (the sweeps of the FP8 tests): block b of x [n, 128]
+ * quantised as oracle_quantize_block into q [n, 128] and s[b]. */
+void oracle_quantize_blocks(const uint16_t* x, int64_t n, uint8_t* q, float* s) {
+#pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < n; b++) oracle_quantize_block(x + 128 * b, q + 128 * b, s + b);
+}
 
 /* Elementwise encoders used by the tests that sweep the E4M3 rounding. */
 void oracle_e4m3_encode_array(const float* v, uint8_t* out, int64_t n) {

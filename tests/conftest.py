@@ -11,6 +11,12 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
     config.addinivalue_line("markers", "slow: long exhaustive sweep, opt-in via MOE_EXHAUSTIVE=1")
+    # the CPU oracle is test infrastructure: build its library variants when
+    # they are missing or older than the source (loading it never compiles)
+    import oracle
+    stale = [v for v in oracle.VARIANTS if oracle.stale(v)]
+    if stale:
+        oracle.build(stale)
 
 
 def pytest_collection_modifyitems(config, items):
