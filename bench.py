@@ -26,6 +26,7 @@ import os
 import re
 import statistics
 import sys
+import subprocess
 import time
 
 import numpy as np
@@ -586,14 +587,27 @@ def copy_bandwidth(nbytes=1 << 30, reps=10):
     return 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
-def cpu_baseline(w, max_tokens):
-    """The CPU oracle (single thread, as it stands) on a bounded token sample of
-    the same workload: routing + dispatch + combine; its experts are replaced by
-    the token rows themselves (identity) so no oracle time goes to them."""
+def _host_cpu():
+    """(logical CPUs this process may run on, CPU model name)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count()
+    model = "unknown"
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except (OSError, subprocess.SubprocessError):
+        pass
+    return n, model
+
+
+def _oracle_legs(ws, x, l):
+    """One oracle pass: (route+dispatch seconds, combine seconds, rows)."""
     import oracle
-    from moe_synth import gen_inputs
-    ws = w.with_(T=min(w.T, max_tokens))
-    x, l = gen_inputs(ws)
     t0 = time.perf_counter()
     idx, wt = oracle.route_topk(l, ws.k)
     d = oracle.dispatch(x, idx, ws.E, ws.groups, ws.row_align, ws.fp8)
@@ -602,13 +616,44 @@ def cpu_baseline(w, max_tokens):
     t2 = time.perf_counter()
     oracle.combine(eo, d.dst_row, wt)
     t3 = time.perf_counter()
-    bd, bc = algorithmic_bytes(ws.T, ws.H, ws.E, ws.k, d.num_rows, ws.fp8)
-    secs = (t1 - t0) + (t3 - t2)
-    return dict(value=round((bd + bc) / secs / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
-                sample=(f"{ws.T} of {w.T} tokens of {w.name} (H={ws.H}, E={ws.E}, k={ws.k}), "
-                        f"single-threaded C oracle, route+dispatch {t1 - t0:.2f} s, "
-                        f"combine {t3 - t2:.2f} s"),
-                seconds=round(secs, 3))
+    return t1 - t0, t3 - t2, d.num_rows
+
+
+def cpu_baseline(w, max_tokens, reps=3):
+    """The CPU oracle as it stands on a bounded token sample of the same
+    workload: routing + dispatch + combine, its experts replaced by the token
+    rows themselves (identity) so no oracle time goes to them. Two builds of
+    the one source: single-threaded, and OpenMP over tokens (the histogram and
+    the scan stay serial) on every host thread it is given. Each leg's time is
+    the median of reps runs; value is the OpenMP build's rate."""
+    import oracle
+    from moe_synth import gen_inputs
+    ws = w.with_(T=min(w.T, max_tokens))
+    x, l = gen_inputs(ws)
+    n_cpu, model = _host_cpu()
+    legs = {}
+    prev = oracle.variant()
+    try:
+        for v in ("plain", "omp"):
+            oracle.set_variant(v)
+            runs = [_oracle_legs(ws, x, l) for _ in range(reps)]
+            td = float(np.median([r[0] for r in runs]))
+            tc = float(np.median([r[1] for r in runs]))
+            bd, bc = algorithmic_bytes(ws.T, ws.H, ws.E, ws.k, runs[0][2], ws.fp8)
+            legs[v] = dict(value=round((bd + bc) / (td + tc) / 1e9, 4), threads=oracle.threads(),
+                           route_dispatch_s=round(td, 4), combine_s=round(tc, 4))
+    finally:
+        oracle.set_variant(prev)
+    par, one = legs["omp"], legs["plain"]
+    return dict(value=par["value"], unit="GB/s", cores=par["threads"], kind="oracle",
+                sample=(f"{ws.T} of {w.T} tokens of {w.name} (H={ws.H}, E={ws.E}, k={ws.k}); "
+                        f"C oracle built with OpenMP, {par['threads']} threads; median of {reps} "
+                        f"runs per leg: route+dispatch {par['route_dispatch_s']:.3f} s, "
+                        f"combine {par['combine_s']:.3f} s"),
+                single_thread=dict(value=one["value"], unit="GB/s", cores=1,
+                                   route_dispatch_s=one["route_dispatch_s"],
+                                   combine_s=one["combine_s"]),
+                host=dict(nproc=n_cpu, cpu_model=model))
 
 
 def summarize(w, r):

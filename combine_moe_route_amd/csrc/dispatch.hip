@@ -20,12 +20,15 @@
 //           tokens' bits). Both fit a byte: at most 64 tokens per tile. In
 //           moe_route_dispatch the same block first routes its tokens (top-k
 //           by sorting networks, topk_sort.h).
-//   scan    one block. The byte counts come into LDS in one batch of 16-byte
-//           loads (in chunks when they exceed 64 KiB); per expert an exclusive
-//           sum over tiles gives each tile's first row inside the expert's
-//           segment (this makes the order stable); the totals, padded to
-//           row_align, are summed over experts into offsets; group offsets are
-//           read off the expert offsets.
+//   scan    up to 32 blocks, each owning a range of tiles. Every block brings
+//           all byte counts into LDS in batches of 16-byte loads (chunks of
+//           64 KiB), sums every expert's total and its prefix up to the
+//           block's first tile, and scans the totals, padded to row_align,
+//           over experts into offsets (the same in every block, so no block
+//           waits for another; block 0 writes counts, offsets and group
+//           offsets). Each block then writes, for its tiles, each tile's
+//           first row inside the expert's segment (this makes the order
+//           stable).
 //   scatter one wave per (token, row chunk): row = segment offset + tile prefix
 //           + in-tile rank; reads each x row once with 16-byte streaming loads
 //           and stores it to its k rows (FP8: one quantisation per token, k

@@ -15,6 +15,7 @@ uint16 bit patterns, E4M3 arrays are uint8 codes.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import subprocess
@@ -68,6 +69,17 @@ def variant() -> str:
     return _variant
 
 
+@contextlib.contextmanager
+def using(variant: str):
+    """Run the enclosed calls on another library variant."""
+    prev = _variant
+    set_variant(variant)
+    try:
+        yield
+    finally:
+        set_variant(prev)
+
+
 def _load():
     if _variant in _libs:
         return _libs[_variant]
@@ -78,6 +90,8 @@ def _load():
     lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     i64, i32 = ctypes.c_int64, ctypes.c_int
+    lib.oracle_threads.argtypes = []
+    lib.oracle_threads.restype = i32
     lib.oracle_route_topk.argtypes = [P, i64, i32, i32, P, P]
     lib.oracle_route_topk.restype = None
     lib.oracle_dispatch.argtypes = [P, P, i64, i32, i32, i32, i32, i32, i32,
@@ -115,6 +129,11 @@ def _load():
     lib.oracle_grouped_gemm_fp8_at.restype = None
     _libs[_variant] = lib
     return lib
+
+
+def threads() -> int:
+    """Host threads the current variant's parallel loops use."""
+    return int(_load().oracle_threads())
 
 
 def _p(a: Optional[np.ndarray]):

@@ -7,7 +7,7 @@
  * share no source. Build: gcc -O2 -std=c11 -fPIC -shared (no fast-math, SSE
  * arithmetic, default round-to-nearest-even mode), single-threaded. The same
  * source is also built with -fopenmp: the only pragmas spread independent
- * per-token (or per-block) iterations over threads; counting, offsets and the
+ * per-token, per-row or per-block iterations over threads; counting, offsets and the
  * stable placement stay serial, and no arithmetic changes.
  *
  * Sources (Perplexity engineering posts):
@@ -45,6 +45,18 @@
 #include <stdint.h>
 #include <string.h>
 #include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Threads the parallel loops below use: 1 unless built with OpenMP. */
+int oracle_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* ---------------------------------------------------------------- bf16 */
 
@@ -276,6 +288,7 @@ void oracle_expert_scale(const void* disp, const float* scales,
                          int64_t num_rows, int H, int E, int fp8, int identity,
                          uint16_t* expert_out) {
     const int nb = H / 128;
+#pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < num_rows; r++) {
         uint16_t* o = expert_out + r * H;
         if (row_src[r] < 0) { memset(o, 0, sizeof(uint16_t) * (size_t)H); continue; }

@@ -49,9 +49,11 @@ def test_kimi_prefill_full_parity(dev):
 
 
 def test_dsv3_prefill_full_size(dev):
-    """Full 16384-token FP8 workload: routing and the whole dispatch layout and
-    payload bit for bit; stand-in experts and combine on a token sample."""
-    from combine_moe_route_amd import moe_combine, moe_harness_expert_scale, moe_route_topk
+    """Full 16384-token FP8 workload: routing, the whole dispatch layout and
+    payload, every stand-in expert row and every combined token, bit for bit
+    (combine within its tolerance). The oracle's combine runs in its OpenMP
+    build."""
+    from combine_moe_route_amd import moe_combine, moe_harness_expert_scale
     c = case_of("dsv3_prefill")
     log(f"[case] {c.label()}")
     x_np = gen_x_bf16(c.T, c.H, c.seed)
@@ -59,23 +61,17 @@ def test_dsv3_prefill_full_size(dev):
     idx_np, w_np = route_parity(logits, c.k, dev)
     ref, bufs = dispatch_parity(x_np, idx_np, c.E, c.groups, c.row_align, c.fp8, dev)
     assert ref.num_rows == 147584
-    # experts on the GPU for every row; oracle experts on the rows of a sample
     idx = torch.from_numpy(idx_np).to(dev)
     eo = moe_harness_expert_scale(bufs, idx, c.E, fp8=True)
-    rng = np.random.default_rng(0)
-    toks = np.sort(rng.choice(c.T, 384, replace=False))
-    rows = np.unique(ref.dst_row[toks].ravel())
-    sub = oracle.Dispatch(ref.out[rows], ref.scales[rows], ref.expert_counts, ref.expert_offsets,
-                          ref.group_offsets, ref.row_src[rows], ref.dst_row, len(rows))
-    eo_ref = oracle.expert_scale(sub, idx_np, c.E, fp8=True)
-    rows_t = torch.from_numpy(rows.astype(np.int64)).to(dev)
-    assert np.array_equal(bf16_to_np(eo[rows_t]), eo_ref)
     y = moe_combine(eo, bufs.dst_row, torch.from_numpy(w_np).to(dev))
-    remap = np.searchsorted(rows, ref.dst_row[toks])
-    y_ref = oracle.combine(eo_ref, remap.astype(np.int32), w_np[toks])
-    ok, within_ulp, exact = combine_within_tolerance(bf16_to_np(y[torch.from_numpy(toks).to(dev)]), y_ref)
+    with oracle.using("omp"):
+        eo_ref = oracle.expert_scale(ref, idx_np, c.E, fp8=True)
+        assert np.array_equal(bf16_to_np(eo[:ref.num_rows]), eo_ref)
+        log("  stand-in experts: every row equal")
+        y_ref = oracle.combine(eo_ref, ref.dst_row, w_np)
+    ok, within_ulp, exact = combine_within_tolerance(bf16_to_np(y), y_ref)
     assert ok.all() and within_ulp.all()
-    log(f"  combine exact on sample {exact:.5f}")
+    log(f"  combine: all {c.T} tokens within tolerance, exact {exact:.5f}")
 
 
 # ----------------------------------------------------------------- edge cases
@@ -215,31 +211,6 @@ def test_fp8_quantiser_domain_sweep(dev):
     idx = np.zeros((x.shape[0], 1), np.int32)
     log(f"  sweep: {x.size} elements, {n} blocks")
     dispatch_parity(x, idx, 1, 1, 1, True, dev)
-
-
-@pytest.mark.slow
-def test_fp8_quantiser_exhaustive_domain(dev):
-    """Every (x, amax) bf16 pair with |x| <= amax, amax > 0 (~2^30 pairs)."""
-    H = 4096
-    chunk = []
-    done = 0
-    for a in range(1, 0x7F80):
-        mags = np.arange(0, a + 1, dtype=np.uint32)
-        vals = np.concatenate([mags, mags[1:] | 0x8000]).astype(np.uint16)
-        pad = (-len(vals)) % 127
-        vals = np.concatenate([vals, np.zeros(pad, np.uint16)]).reshape(-1, 127)
-        chunk.append(np.concatenate([np.full((len(vals), 1), a, np.uint16), vals], axis=1))
-        if sum(len(c) for c in chunk) >= (1 << 18) or a == 0x7F7F:
-            b = np.concatenate(chunk)
-            if a == 0x7F7F:   # pad the last rows with all-zero blocks
-                b = np.concatenate([b, np.zeros(((-len(b)) % (H // 128), 128), np.uint16)])
-            n = len(b) // (H // 128) * (H // 128)
-            rest = b[n:]
-            x = b[:n].reshape(-1, H)
-            dispatch_parity(x, np.zeros((x.shape[0], 1), np.int32), 1, 1, 1, True, dev)
-            done += n
-            chunk = [rest] if len(rest) else []
-            log(f"  exhaustive: amax up to {a:#06x}, {done} blocks")
 
 
 @pytest.mark.parametrize("E", [1, 2, 3, 4, 5, 7, 8, 9, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128,
