@@ -20,8 +20,8 @@
 // shapes are described at Shape below). Each 128-wide k-block of both
 // operands and of the activation scales goes from memory straight into LDS
 // with buffer_load ... lds (no staging registers), into a ring of stages, and
-// the loads of a later k-block are issued in pieces between the MFMA groups
-// of the current one, so their issue never holds the matrix pipe. One barrier
+// the loads of a later k-block are issued at the top of the current one,
+// right after the barrier that frees their stage. One barrier
 // per k-block; the wait before it counts this wave's outstanding DMA
 // explicitly, because the fence of __syncthreads would drain the prefetch as
 // well.
@@ -73,12 +73,19 @@ __global__ __launch_bounds__(kTileListThreads) void k_gemm_tiles(
 }
 
 // LDS layout of a staged k-block: row-major 128-byte rows of 16-byte chunks,
-// chunk c of row r stored at chunk c ^ ((r >> 1) & 7). A fragment read has 16
-// lanes on 16 consecutive rows at the same logical chunk; even rows fall in
-// one half of the 64 banks and odd rows in the other, and the XOR spreads
-// each half's 8 rows over distinct 16-byte bank groups: no conflicts.
+// chunk c of row r stored at chunk c ^ key(r), key(r) = (r & 7) ^ ((r >> 3) & 1).
+// A fragment read has lanes on consecutive rows at the same logical chunk.
+// Any 8 consecutive rows from a multiple of 8 get 8 distinct physical chunks,
+// so 8 lanes cover 128 bytes of distinct banks; and within 16 rows from a
+// multiple of 16 the even rows, like the odd ones, also get 8 distinct chunks,
+// so 16 lanes cover 256 bytes of distinct banks when a row's two halves of
+// the bank space alternate. (A swizzle on (r >> 1) alone left rows r and r + 1
+// on the same chunk; the counters showed about one bank-conflict cycle per LDS
+// access.)
+__device__ __forceinline__ int chunk_key(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
 __device__ __forceinline__ int swz(int row, int chunk) {
-    return row * kBK + ((chunk ^ ((row >> 1) & 7)) << 4);
+    return row * kBK + ((chunk ^ chunk_key(row)) << 4);
 }
 
 [[maybe_unused]] __device__ __forceinline__ i32x8 frag(const uint8_t* s, int row, int half) {
@@ -169,12 +176,12 @@ __device__ __forceinline__ void gemm_body(
 #pragma unroll
     for (int i = 0; i < SH::kAChunks; i++) {
         const int p = (wave * SH::kAChunks + i) * 64 + lane, r = p >> 3;
-        a_goff[i] = r * K + (((p & 7) ^ ((r >> 1) & 7)) << 4);
+        a_goff[i] = r * K + (((p & 7) ^ chunk_key(r)) << 4);
     }
 #pragma unroll
     for (int i = 0; i < 4; i++) {
         const int p = (wave * 4 + i) * 64 + lane, r = p >> 3;
-        w_goff[i] = r * K + (((p & 7) ^ ((r >> 1) & 7)) << 4);
+        w_goff[i] = r * K + (((p & 7) ^ chunk_key(r)) << 4);
     }
     // Scale DMA: lane l fetches the scale of the wave's row l (rows past the
     // tile's end read 0 through the descriptor bound).
@@ -228,13 +235,15 @@ __device__ __forceinline__ void gemm_body(
         for (int j = 0; j < 4 * SH::kHalves; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int half = lane >> 4;
-    // One k-block from stage st; the pieces of the DMA into stage nst (k-block
-    // nb) are issued between the first half's MFMA groups.
+    // One k-block from stage st; the DMA into stage nst (k-block nb) is
+    // issued first.
     auto compute = [&](auto st, auto nst, int nb) {
         constexpr int S = decltype(st)::value;
         const uint8_t* A = stageA(st);
         const uint8_t* W = stageW(st);
         const float* Ssc = stageS(st) + wave * 64;
+#pragma unroll
+        for (int q = 0; q < 4; q++) issue_part(nst, nb, q);
         float f[4];
 #pragma unroll
         for (int i = 0; i < 4; i++) f[i] = Ssc[i * 16 + (lane & 15)] * sw[S];
@@ -257,7 +266,10 @@ __device__ __forceinline__ void gemm_body(
                 for (int j = 0; j < 4; j++)
                     cur[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                         wf[j], xf[i], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-                if (hh == 0) issue_part(nst, nb, i);
+                // keep the promotion of the previous group after this group's
+                // MFMAs: hoisted above them, it would wait for the previous
+                // group's results instead of running beside this group
+                __builtin_amdgcn_sched_barrier(0);
                 if (i > 0) {
 #pragma unroll
                     for (int j = 0; j < 4; j++)
