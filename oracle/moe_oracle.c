@@ -342,6 +342,7 @@ void oracle_e4m3_encode_array(const float* v, uint8_t* out, int64_t n) {
 }
 
 void oracle_e4m3_encode_bits(uint32_t start, int64_t count, uint8_t* out) {
+#pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < count; i++) {
         uint32_t u = start + (uint32_t)i;
         float f;

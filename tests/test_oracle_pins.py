@@ -155,16 +155,29 @@ def test_e4m3_encode_saturates_and_keeps_sign():
     assert oracle.e4m3_encode(3 * 2.0 ** -10) == 0x02    # tie between 1 and 2 (x 2^-9) -> 2
 
 
-@pytest.mark.slow
 def test_e4m3_encode_all_fp32_patterns():
-    """All 2^32 fp32 bit patterns against the nearest-code search (minutes)."""
-    step = 1 << 26
-    for start in range(0, 1 << 32, step):
-        got = oracle.e4m3_encode_bits(start, step)
-        v = (np.arange(start, start + step, dtype=np.uint64).astype(np.uint32)).view(np.float32)
-        fin = np.isfinite(v)
-        want = nearest_code(v[fin].astype(np.float64))
-        assert np.array_equal(got[fin], want), hex(start)
+    """All 2^32 fp32 bit patterns (the finite ones) through the encoder.
+    Magnitudes below 2^-10 (under half the smallest subnormal code, 2^-9) must
+    give a signed zero and magnitudes above 448 the saturated code; every
+    pattern in between goes through the nearest-code search. The encoder runs
+    in the oracle's OpenMP build (same source)."""
+    step = 1 << 26                                   # a chunk never straddles the sign bit
+    lo_mag, hi_mag, inf_mag = 0x3A800000, 0x43E00000, 0x7F800000   # 2^-10, 448, inf
+    with oracle.using("omp"):
+        for start in range(0, 1 << 32, step):
+            got = oracle.e4m3_encode_bits(start, step)
+            sign = 0x80 if start >> 31 else 0x00
+            m0 = start & 0x7FFFFFFF                      # magnitudes m0 .. m0 + step - 1, in order
+            i_lo = min(max(lo_mag - m0, 0), step)        # first index with magnitude >= 2^-10
+            i_hi = min(max(hi_mag + 1 - m0, 0), step)    # first index with magnitude > 448
+            i_inf = min(max(inf_mag - m0, 0), step)      # first non-finite index
+            assert np.all(got[:i_lo] == sign), hex(start)
+            assert np.all(got[i_hi:i_inf] == (0x7E | sign)), hex(start)
+            if i_hi > i_lo:
+                u = np.arange(i_lo, i_hi, dtype=np.uint32) + np.uint32(start)
+                want = nearest_code(u.view(np.float32).astype(np.float64))
+                bad = np.flatnonzero(got[i_lo:i_hi] != want)
+                assert bad.size == 0, hex(start + i_lo + int(bad[0]))
 
 
 # ----------------------------------------------------------------- bf16
