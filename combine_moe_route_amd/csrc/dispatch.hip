@@ -37,7 +37,10 @@
 // Small batches (at most 64 tiles and 4096 tile counts, e.g. 128-token decode)
 // skip the scan launch: every scatter block stages the byte counts itself and
 // builds the tile prefixes and offsets in LDS while its x row is in flight
-// (block 0 writes the count and offset outputs).
+// (block 0 writes the count and offset outputs). In moe_route_dispatch, small
+// batches with few experts (E <= 48) skip the counting launch as well: every
+// scatter block routes the whole batch in LDS (route_block_small), so
+// dispatch is one launch.
 #include "moe_device.h"
 #include "launch.h"
 #include "topk_sort.h"
@@ -439,6 +442,64 @@ __device__ void inline_scan(const uint8_t* __restrict__ counts, int tiles, int E
     }
 }
 
+// Whole-batch routing inside one block, for decode batches with few experts
+// (E <= 48, so one lane holds a token's whole logit row; T <= the block's
+// threads; T * k <= kSmallPairs). Every block routes every token (a few
+// hundred logits per block, served from L2 after the first block), keeps the
+// experts in LDS, counts them per expert and scans the padded counts into
+// segment offsets; block 0 writes topk_idx / topk_w, the counts and the
+// offsets. A token's rank inside an expert's segment is the number of earlier
+// (token, slot) pairs with that expert (the stable order), counted by the
+// token's wave with ballots. Dispatch is then a single launch.
+constexpr int kSmallExperts = 4 * kRouteChunks;   // 48
+constexpr int kSmallTokens = 256;
+constexpr int kSmallPairs = 1024;
+
+struct SmallLds {
+    int32_t ids[kSmallPairs];      // expert of pair t * k + j
+    int32_t cnt[kWave];
+    int32_t off[kWave + 1];
+};
+
+template <int K>
+__device__ void route_block_small(const float* __restrict__ logits, int T, int E, int k,
+                                  int row_align, int groups, bool write_out,
+                                  int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+                                  int32_t* __restrict__ g_counts, int32_t* __restrict__ g_offsets,
+                                  int32_t* __restrict__ g_goffs, SmallLds& L) {
+    const int tid = threadIdx.x;
+    if (tid < kWave) L.cnt[tid] = 0;
+    __syncthreads();
+    if (tid < T) {
+        double list[K];
+        route_token<1, K>(logits + (int64_t)tid * E, true, E, 0, list);
+#pragma unroll
+        for (int j = 0; j < K; j++)
+            if (j < k) {
+                const int e = cand_expert(list[j]);
+                L.ids[tid * k + j] = e;
+                atomicAdd(&L.cnt[e], 1);
+            }
+        if (write_out) write_route<1, K>(list, 0, tid, tid, E, k, k, 0, 0.0f, topk_idx, topk_w, nullptr);
+    }
+    __syncthreads();
+    if (tid < kWave) {   // wave 0: exclusive scan of the padded counts over experts
+        const int c = tid < E ? L.cnt[tid] : 0;
+        const int padded = (c + row_align - 1) / row_align * row_align;
+        const int incl = wave_inclusive_sum(padded);
+        L.off[tid] = incl - padded;
+        if (tid == kWave - 1) L.off[E] = incl;
+        if (write_out && tid < E) {
+            g_counts[tid] = c;
+            g_offsets[tid] = incl - padded;
+        }
+        if (write_out && tid == kWave - 1) g_offsets[E] = incl;
+    }
+    __syncthreads();
+    if (write_out && g_goffs != nullptr)
+        for (int gi = tid; gi <= groups; gi += blockDim.x) g_goffs[gi] = L.off[gi * (E / groups)];
+}
+
 constexpr int kScatterThreads = 256;
 
 // Zero the pad rows of one expert's segment, or the part of them this
@@ -496,6 +557,28 @@ __device__ __forceinline__ void slot_rows(const int32_t* __restrict__ topk_idx,
     }
 }
 
+// Destination rows of slots j0 .. j0+7 of token t from the block-local
+// routing: segment offset + the number of earlier pairs with the same expert.
+// The whole wave takes part (t is wave-uniform).
+__device__ __forceinline__ int row_small(const SmallLds& L, int p, int64_t max_rows) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int e = L.ids[p];
+    int rank = 0;
+    for (int q0 = 0; q0 < p; q0 += kWave) {
+        const int q = q0 + lane;
+        rank += __popcll(__ballot(q < p && L.ids[q] == e));
+    }
+    const int rr = L.off[e] + rank;
+    return (rr < 0 || rr >= max_rows) ? -1 : rr;
+}
+
+__device__ __forceinline__ void slot_rows_small(const SmallLds& L, int64_t t, int j0, int k,
+                                                int64_t max_rows, int r[8]) {
+#pragma unroll
+    for (int jj = 0; jj < 8; jj++)
+        r[jj] = j0 + jj < k ? row_small(L, (int)t * k + j0 + jj, max_rows) : -1;
+}
+
 // The wave that owns slots j0 .. j0+7 publishes dst_row and row_src for them.
 __device__ __forceinline__ void publish_rows(int lane, int64_t p0, int j0, int k, const int r[8],
                                              int32_t* __restrict__ dst_row,
@@ -522,7 +605,21 @@ struct ScanView {
     const int32_t* tb;
 };
 
-template <bool INLINE>
+// Where the scatter gets its rows from.
+enum ScatterMode {
+    kScanned = 0,   // the scan kernel ran: offsets and tile prefixes in global memory
+    kInline = 1,    // the block scans the tile counts itself (small batches)
+    kRouted = 2     // the block routes the whole batch itself (small batches, E <= 48)
+};
+
+// Routing inputs and outputs of the kRouted mode.
+struct RouteArgs {
+    const float* logits;
+    int32_t* topk_idx;
+    float* topk_w;
+};
+
+template <int MODE, int KL>
 __global__ __launch_bounds__(kScatterThreads) void k_scatter_bf16(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ topk_idx,
     const uint8_t* __restrict__ tile_rank, const int32_t* __restrict__ tile_base,
@@ -531,7 +628,7 @@ __global__ __launch_bounds__(kScatterThreads) void k_scatter_bf16(
     int32_t* __restrict__ expert_counts, int32_t* __restrict__ expert_offsets,
     int64_t T, int H, int E, int k, int TT, int64_t max_rows, int pad_blocks,
     int pad_blocks_per_expert, int pad_rows_per_block, unsigned char* __restrict__ out,
-    int32_t* __restrict__ row_src, int32_t* __restrict__ dst_row) {
+    int32_t* __restrict__ row_src, int32_t* __restrict__ dst_row, RouteArgs ra) {
     const int lane = threadIdx.x & (kWave - 1);
     const int U = H / 8;                           // 16-byte units per row
     const int CW = (U + kWave - 1) / kWave;        // waves per token
@@ -541,15 +638,21 @@ __global__ __launch_bounds__(kScatterThreads) void k_scatter_bf16(
     const int64_t t = pad_block ? T : gw / CW;
     const int chunk = (int)(gw - t * CW);
     const int u = chunk * kWave + lane;
-    // the x row first, so that its load overlaps the inline scan
+    // the x row first, so that its load overlaps the scan or the routing
     uint4 a = make_uint4(0u, 0u, 0u, 0u);
     if (t < T) a = load16_nt(range_rsrc(x + t * (int64_t)H, 2 * H), 16 * u);
     ScanView sv{expert_offsets, expert_counts, tile_base};
-    if constexpr (INLINE) {
+    __shared__ SmallLds Ls;
+    if constexpr (MODE == kInline) {
         __shared__ InlineLds L;
         inline_scan(tile_counts, tiles, E, row_align, groups, blockIdx.x == 0, expert_counts,
                     expert_offsets, group_offsets, L);
         sv = ScanView{L.off, L.tot, L.tb};
+    } else if constexpr (MODE == kRouted) {
+        route_block_small<KL>(ra.logits, (int)T, E, k, row_align, groups, blockIdx.x == 0,
+                              ra.topk_idx, ra.topk_w, expert_counts, expert_offsets,
+                              group_offsets, Ls);
+        sv = ScanView{Ls.off, Ls.cnt, nullptr};
     }
     if (pad_block) {
         zero_pad_rows(blockIdx.x, pad_blocks_per_expert, pad_rows_per_block, H, false, max_rows,
@@ -558,10 +661,12 @@ __global__ __launch_bounds__(kScatterThreads) void k_scatter_bf16(
     }
     if (t >= T) return;
     const int64_t p0 = t * k;
-    const int32_t* tb = sv.tb + (t / TT) * E;
     for (int j0 = 0; j0 < k; j0 += 8) {
         int r[8];
-        slot_rows(topk_idx, tile_rank, sv.off, tb, p0, j0, k, E, max_rows, r);
+        if constexpr (MODE == kRouted)
+            slot_rows_small(Ls, t, j0, k, max_rows, r);
+        else
+            slot_rows(topk_idx, tile_rank, sv.off, sv.tb + (t / TT) * E, p0, j0, k, E, max_rows, r);
         if (chunk == 0) publish_rows(lane, p0, j0, k, r, dst_row, row_src);
         if (u < U) {
 #pragma unroll
@@ -579,7 +684,7 @@ __global__ __launch_bounds__(kScatterThreads) void k_scatter_bf16(
 // to each destination row, and its 1x128 scales are staged in LDS and written
 // to each row's scale segment with one contiguous store (instead of many small
 // pieces from different waves, which cost HBM read-modify-write cycles).
-template <bool INLINE>
+template <int MODE, int KL>
 __global__ __launch_bounds__(1024) void k_scatter_fp8(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ topk_idx,
     const uint8_t* __restrict__ tile_rank, const int32_t* __restrict__ tile_base,
@@ -588,7 +693,8 @@ __global__ __launch_bounds__(1024) void k_scatter_fp8(
     int32_t* __restrict__ expert_counts, int32_t* __restrict__ expert_offsets,
     int64_t T, int H, int E, int k, int TT, int64_t max_rows, int pad_blocks,
     int pad_blocks_per_expert, int pad_rows_per_block, unsigned char* __restrict__ out,
-    float* __restrict__ scales, int32_t* __restrict__ row_src, int32_t* __restrict__ dst_row) {
+    float* __restrict__ scales, int32_t* __restrict__ row_src, int32_t* __restrict__ dst_row,
+    RouteArgs ra) {
     extern __shared__ float s_scale[];             // [H / 128]
     const bool pad_block = (int)blockIdx.x < pad_blocks;
     const int64_t t = pad_block ? 0 : blockIdx.x - pad_blocks;
@@ -599,19 +705,25 @@ __global__ __launch_bounds__(1024) void k_scatter_fp8(
     const int CW = (U + kWave - 1) / kWave;
     const int nb = H / 128;
     const auto xr = range_rsrc(x + t * (int64_t)H, pad_block ? 0 : 2 * H);
-    // the first chunk of the x row first, so that its load overlaps the
-    // inline scan
+    // the first chunk of the x row first, so that its load overlaps the scan
+    // or the routing
     uint4 a0 = make_uint4(0u, 0u, 0u, 0u), b0 = a0;
     if (!pad_block && w < CW) {
         a0 = load16_nt(xr, 32 * (w * kWave + lane));
         b0 = load16_nt(xr, 32 * (w * kWave + lane) + 16);
     }
     ScanView sv{expert_offsets, expert_counts, tile_base};
-    if constexpr (INLINE) {
+    __shared__ SmallLds Ls;
+    if constexpr (MODE == kInline) {
         __shared__ InlineLds L;
         inline_scan(tile_counts, tiles, E, row_align, groups, blockIdx.x == 0, expert_counts,
                     expert_offsets, group_offsets, L);
         sv = ScanView{L.off, L.tot, L.tb};
+    } else if constexpr (MODE == kRouted) {
+        route_block_small<KL>(ra.logits, (int)T, E, k, row_align, groups, blockIdx.x == 0,
+                              ra.topk_idx, ra.topk_w, expert_counts, expert_offsets,
+                              group_offsets, Ls);
+        sv = ScanView{Ls.off, Ls.cnt, nullptr};
     }
     if (pad_block) {
         zero_pad_rows(blockIdx.x, pad_blocks_per_expert, pad_rows_per_block, H, true, max_rows,
@@ -619,7 +731,7 @@ __global__ __launch_bounds__(1024) void k_scatter_fp8(
         return;
     }
     const int64_t p0 = t * k;
-    const int32_t* tb = sv.tb + (t / TT) * E;
+    const int32_t* tb = MODE == kRouted ? nullptr : sv.tb + (t / TT) * E;
 
     for (int chunk = w; chunk < CW; chunk += W) {
         const int u = chunk * kWave + lane;
@@ -643,7 +755,10 @@ __global__ __launch_bounds__(1024) void k_scatter_fp8(
         if (u < U && (u & 7) == 0) s_scale[u >> 3] = s;
         for (int j0 = 0; j0 < k; j0 += 8) {
             int r[8];
-            slot_rows(topk_idx, tile_rank, sv.off, tb, p0, j0, k, E, max_rows, r);
+            if constexpr (MODE == kRouted)
+                slot_rows_small(Ls, t, j0, k, max_rows, r);
+            else
+                slot_rows(topk_idx, tile_rank, sv.off, tb, p0, j0, k, E, max_rows, r);
             if (chunk == 0) publish_rows(lane, p0, j0, k, r, dst_row, row_src);
             if (u < U) {
 #pragma unroll
@@ -656,9 +771,14 @@ __global__ __launch_bounds__(1024) void k_scatter_fp8(
     __syncthreads();
     // scale segments: wave w writes the segments of slots w, w+W, ...
     for (int j = w; j < k; j += W) {
-        const int e = topk_idx[p0 + j];
-        if ((unsigned)e >= (unsigned)E) continue;
-        const int rr = sv.off[e] + tb[e] + tile_rank[p0 + j];
+        int rr;
+        if constexpr (MODE == kRouted) {
+            rr = row_small(Ls, (int)p0 + j, max_rows);
+        } else {
+            const int e = topk_idx[p0 + j];
+            if ((unsigned)e >= (unsigned)E) continue;
+            rr = sv.off[e] + tb[e] + tile_rank[p0 + j];
+        }
         if (rr < 0 || rr >= max_rows) continue;
         for (int i = lane; i < nb; i += kWave) scales[(int64_t)rr * nb + i] = s_scale[i];
     }
@@ -701,6 +821,11 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream, LaunchInfo
     const int64_t scan_blocks = tiles < 1 ? 1 : tiles < kScanBlocks ? tiles : kScanBlocks;
     // small batches scan inside the scatter (there must be scatter blocks)
     const bool inline_scan_ok = a.T > 0 && tiles <= kInlineTiles && tiles * a.E <= kInlineCells;
+    // small batches with few experts: every scatter block routes the whole
+    // batch, so dispatch is one launch (the scatter's blocks have at least
+    // kSmallTokens threads)
+    const bool routed = fused && a.T > 0 && a.E <= kSmallExperts && a.T <= kSmallTokens &&
+                        a.T * a.k <= kSmallPairs;
 
     int pad_per_expert = 0, pad_rows_per_block = 0;
     if (a.row_align > 1 && a.T > 0) {
@@ -721,19 +846,22 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream, LaunchInfo
     if (route_first)
         (void)launch_route_topk(a.logits, a.T, a.E, a.k, 0, 0.0f, const_cast<int32_t*>(a.topk_idx),
                                 a.topk_w, stream, &route_info, false);
+    const char* scatter_name = routed ? "route+scan+scatter" : inline_scan_ok ? "scan+scatter" : "scatter";
     if (info) {
         if (route_first) info[nk++] = LaunchInfo{route_info.grid, route_info.block, route_info.lds,
                                                  route_info.param, "route"};
-        info[nk++] = LaunchInfo{tiles, count_threads, count_lds, fused ? S : TT,
-                                fused ? "route_count" : "count"};
-        if (!inline_scan_ok) info[nk++] = LaunchInfo{scan_blocks, kScanThreads, 0, tiles, "scan"};
+        if (!routed)
+            info[nk++] = LaunchInfo{tiles, count_threads, count_lds, fused ? S : TT,
+                                    fused ? "route_count" : "count"};
+        if (!routed && !inline_scan_ok)
+            info[nk++] = LaunchInfo{scan_blocks, kScanThreads, 0, tiles, "scan"};
         info[nk++] = a.fp8 ? LaunchInfo{scatter_blocks, fp8_threads,
                                         (size_t)(a.H / 128) * sizeof(float), fp8_waves,
-                                        inline_scan_ok ? "scan+scatter" : "scatter"}
+                                        scatter_name}
                            : LaunchInfo{scatter_blocks, kScatterThreads, 0, bf16_waves_per_token,
-                                        inline_scan_ok ? "scan+scatter" : "scatter"};
+                                        scatter_name};
     } else {
-        nk = (route_first ? 1 : 0) + (inline_scan_ok ? 2 : 3);
+        nk = routed ? 1 : (route_first ? 1 : 0) + (inline_scan_ok ? 2 : 3);
     }
     if (n) *n = nk;
     if (!run) return hipSuccess;
@@ -745,7 +873,7 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream, LaunchInfo
         if (err != hipSuccess) return err;
     }
     const CountArgs c{a.T, a.E, a.k, TT, tiles, a.tile_counts, a.tile_rank};
-    if (tiles > 0) {
+    if (tiles > 0 && !routed) {
         if (fused) {
             switch (route_list_len(a.k)) {
                 case 2: launch_route_count_k<2>(S, a, c, tiles, count_threads, count_lds, stream); break;
@@ -757,7 +885,7 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream, LaunchInfo
         }
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
-    if (!inline_scan_ok) {
+    if (!routed && !inline_scan_ok) {
         k_scan<<<dim3((unsigned)scan_blocks), kScanThreads, 0, stream>>>(
             a.tile_counts, tiles, a.E, a.row_align, a.groups, a.tile_base, a.expert_counts,
             a.expert_offsets, a.group_offsets);
@@ -768,21 +896,27 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream, LaunchInfo
     unsigned char* out = static_cast<unsigned char*>(a.out);
     const uint16_t* x = static_cast<const uint16_t*>(a.x);
     if (scatter_blocks == 0) return hipSuccess;
+    const RouteArgs ra{a.logits, const_cast<int32_t*>(a.topk_idx), a.topk_w};
+    const int kl = route_list_len(a.k);
     if (a.fp8) {
         const size_t lds = (size_t)(a.H / 128) * sizeof(float);
-        auto kern = inline_scan_ok ? k_scatter_fp8<true> : k_scatter_fp8<false>;
+        auto kern = routed ? (kl == 2 ? k_scatter_fp8<kRouted, 2>
+                              : kl == 4 ? k_scatter_fp8<kRouted, 4> : k_scatter_fp8<kRouted, 8>)
+                    : inline_scan_ok ? k_scatter_fp8<kInline, 2> : k_scatter_fp8<kScanned, 2>;
         kern<<<dim3((unsigned)scatter_blocks), dim3(fp8_threads), lds, stream>>>(
             x, a.topk_idx, a.tile_rank, a.tile_base, a.tile_counts, (int)tiles, a.row_align,
             a.groups, a.group_offsets, a.expert_counts, a.expert_offsets, a.T, a.H, a.E, a.k, TT,
             a.max_rows, (int)pad_blocks, pad_per_expert, pad_rows_per_block, out, a.out_scales,
-            a.row_src, a.dst_row);
+            a.row_src, a.dst_row, ra);
     } else {
-        auto kern = inline_scan_ok ? k_scatter_bf16<true> : k_scatter_bf16<false>;
+        auto kern = routed ? (kl == 2 ? k_scatter_bf16<kRouted, 2>
+                              : kl == 4 ? k_scatter_bf16<kRouted, 4> : k_scatter_bf16<kRouted, 8>)
+                    : inline_scan_ok ? k_scatter_bf16<kInline, 2> : k_scatter_bf16<kScanned, 2>;
         kern<<<dim3((unsigned)scatter_blocks), dim3(kScatterThreads), 0, stream>>>(
             x, a.topk_idx, a.tile_rank, a.tile_base, a.tile_counts, (int)tiles, a.row_align,
             a.groups, a.group_offsets, a.expert_counts, a.expert_offsets, a.T, a.H, a.E, a.k, TT,
             a.max_rows, (int)pad_blocks, pad_per_expert, pad_rows_per_block, out, a.row_src,
-            a.dst_row);
+            a.dst_row, ra);
     }
     return hipGetLastError();
 }

@@ -160,7 +160,8 @@ size_t moe_dispatch_workspace_bytes(int64_t T, int E, int k, int groups);
  * Rows at and beyond expert_offsets[E] are left untouched. max_rows is
  * moe_dispatch_max_rows(T, E, k, row_align). T == 0 writes zero counts and
  * offsets. Three kernels: per-tile counts and ranks, the scan into offsets,
- * the rows.
+ * the rows (two for batches of at most 64 count tiles, whose row kernel
+ * does the scan).
  */
 int moe_dispatch(const void* x, const int32_t* topk_idx,
                  int64_t T, int H, int E, int k, int groups, int row_align,
@@ -175,8 +176,11 @@ int moe_dispatch(const void* x, const int32_t* topk_idx,
  * mixture-of-experts communication", Introduction) feed the counts, offsets
  * and packing of "Enabling trillion-parameter models on AWS EFA", Dispatch
  * and Combine. When k <= 8, E <= 768, E % 4 == 0 and logits is 16-byte
- * aligned, routing runs inside the counting kernel (three launches in all);
- * otherwise moe_route_topk's kernel runs first (four launches).
+ * aligned, routing runs inside the counting kernel (three launches in all,
+ * two for batches of at most 64 count tiles); if besides E <= 48, T <= 256
+ * and T * k <= 1024, every block of the packing kernel routes the whole
+ * batch itself and the call is one launch. Otherwise moe_route_topk's
+ * kernel runs first (four launches).
  *
  *   logits         device fp32 [T, E], finite, 4-byte aligned
  *   topk_idx       device int32 [T, k] out (as moe_route_topk), then read by

@@ -100,6 +100,44 @@ def test_fused_shapes(dev, T, H, E, k, G, A, fp8):
     fused_case(T, H, E, k, G, A, fp8, seed=T + E, dev=dev)
 
 
+@pytest.mark.parametrize("T,H,E,k,G,A,fp8", [
+    (256, 256, 48, 4, 4, 8, True),        # largest T and E of the single-launch path, pad rows
+    (128, 4096, 8, 8, 2, 1, False),       # k == E, T * k = 1024 pairs (the limit)
+    (200, 136, 16, 5, 1, 1, False),       # ragged row units, K = 8 list with k = 5
+    (64, 128, 4, 4, 1, 128, True),        # k == E == 4, 124 pad rows per expert
+    (1, 8, 4, 1, 1, 1, False),            # one token, k = 1
+    (257, 256, 48, 4, 4, 8, True),        # one token over: counting kernel + inline scan
+    (128, 256, 52, 2, 1, 1, False),       # E over 48: counting kernel + inline scan
+], ids=lambda v: str(v))
+def test_single_launch_shapes(dev, T, H, E, k, G, A, fp8):
+    """Small batches with few experts: moe_route_dispatch is one launch in
+    which every block routes the whole batch (the last two cases sit just past
+    its limits)."""
+    fused_case(T, H, E, k, G, A, fp8, seed=7 * T + E, dev=dev)
+
+
+def test_single_launch_ties(dev):
+    """Tied and signed-zero logits on the single-launch path: the lower
+    expert ranks first and the stable row order holds."""
+    from combine_moe_route_amd import alloc_dispatch, moe_route_dispatch
+    rng = np.random.default_rng(5)
+    for E, k, T in [(8, 2, 256), (16, 4, 200), (48, 8, 128)]:
+        l = (np.round(rng.standard_normal((T, E)) * 2) / 4).astype(np.float32)
+        l[0] = 0.0
+        l[1, ::2] = -0.0
+        x_np = gen_x_bf16(T, 128, 5)
+        ri, rw = oracle.route_topk(l, k)
+        gi, gw, b = moe_route_dispatch(torch.from_numpy(l).to(dev), to_dev_bf16(x_np, dev), k,
+                                       1, 1, False, alloc_dispatch(T, 128, E, k, 1, 1, False, dev))
+        torch.cuda.synchronize()
+        assert np.array_equal(gi.cpu().numpy(), ri), (E, k)
+        assert np.all(np.abs(gw.cpu().numpy() - rw) <= 1e-5 * np.abs(rw))
+        ref = oracle.dispatch(x_np, ri, E)
+        assert np.array_equal(b.dst_row.cpu().numpy(), ref.dst_row)
+        assert np.array_equal(b.row_src[:ref.num_rows].cpu().numpy(), ref.row_src)
+        assert np.array_equal(bf16_to_np(b.out[:ref.num_rows]), ref.out)
+
+
 def test_fused_unaligned_logits_fall_back(dev):
     """Logits not 16-byte aligned: the route kernel runs first."""
     T, E, k = 300, 256, 8
