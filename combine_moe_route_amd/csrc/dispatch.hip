@@ -394,9 +394,30 @@ __device__ void inline_scan(const uint8_t* __restrict__ counts, int tiles, int E
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
     const int E4 = (E + 3) & ~3;
-    for (int i = tid; i < tiles * E; i += NT) {
-        const int b = i / E;
-        L.tb[i] = counts[b * E4 + (i - b * E)];
+    // stage the byte counts as 32-bit words (rows are padded to 4 bytes and
+    // the array is 4-byte aligned), every load of a batch issued before any
+    // LDS store, so that the staging costs one memory round trip
+    constexpr int kBatch = 4;
+    const uint32_t* words = reinterpret_cast<const uint32_t*>(counts);
+    const int nwords = tiles * E4 / 4;
+    for (int w0 = 0; w0 < nwords; w0 += kBatch * NT) {
+        uint32_t v[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; i++) {
+            const int w = w0 + i * NT + tid;
+            v[i] = w < nwords ? words[w] : 0u;
+        }
+#pragma unroll
+        for (int i = 0; i < kBatch; i++) {
+            const int w = w0 + i * NT + tid;
+            if (w < nwords) {
+                const int b = (4 * w) / E4;
+                const int c0 = 4 * w - b * E4;
+#pragma unroll
+                for (int q = 0; q < 4; q++)
+                    if (c0 + q < E) L.tb[b * E + c0 + q] = byte_of(v[i], q);
+            }
+        }
     }
     __syncthreads();
     for (int e = tid; e < E; e += NT) {
