@@ -558,8 +558,25 @@ __device__ void zero_pad_rows(int pb, int pad_blocks_per_expert, int pad_rows_pe
 
 constexpr int kScatterWaves = kScatterThreads / kWave;
 
+// Experts and in-tile ranks of slots j0 .. j0+7 of the token whose first
+// slot is p0 (e = -1 past k). The token is wave-uniform; both loads are issued
+// together, and the kernels issue them before the offsets are ready.
+__device__ __forceinline__ void load_slots(const int32_t* __restrict__ topk_idx,
+                                           const uint8_t* __restrict__ tile_rank, int64_t p0,
+                                           int j0, int k, int e[8], int rk[8]) {
+#pragma unroll
+    for (int jj = 0; jj < 8; jj++) {
+        const bool live = j0 + jj < k;
+        e[jj] = live ? topk_idx[p0 + j0 + jj] : -1;
+        rk[jj] = live ? tile_rank[p0 + j0 + jj] : 0;
+    }
+}
+
 // Destination rows of slots j0 .. j0+7 of token t: the segment offset + the
 // tile's first row in the segment (tb) + in-tile rank; -1 for dropped slots.
+// The rank is read only for a live expert. (Loading experts and ranks
+// together, as load_slots does, made the prefill-sized bf16 scatter 6 %
+// slower.)
 __device__ __forceinline__ void slot_rows(const int32_t* __restrict__ topk_idx,
                                           const uint8_t* __restrict__ tile_rank,
                                           const int32_t* __restrict__ offsets,
@@ -574,6 +591,21 @@ __device__ __forceinline__ void slot_rows(const int32_t* __restrict__ topk_idx,
                 const int rr = offsets[e] + tb[e] + tile_rank[p0 + j0 + jj];
                 r[jj] = (rr < 0 || rr >= max_rows) ? -1 : rr;   // never write outside
             }
+        }
+    }
+}
+
+// The same from experts and ranks already loaded (load_slots).
+__device__ __forceinline__ void slot_rows(const int e[8], const int rk[8],
+                                          const int32_t* __restrict__ offsets,
+                                          const int32_t* __restrict__ tb, int E, int64_t max_rows,
+                                          int r[8]) {
+#pragma unroll
+    for (int jj = 0; jj < 8; jj++) {
+        r[jj] = -1;
+        if ((unsigned)e[jj] < (unsigned)E) {
+            const int rr = offsets[e[jj]] + tb[e[jj]] + rk[jj];
+            r[jj] = (rr < 0 || rr >= max_rows) ? -1 : rr;   // never write outside
         }
     }
 }
@@ -661,7 +693,17 @@ __global__ __launch_bounds__(kScatterThreads) void k_scatter_bf16(
     const int u = chunk * kWave + lane;
     // the x row first, so that its load overlaps the scan or the routing
     uint4 a = make_uint4(0u, 0u, 0u, 0u);
-    if (t < T) a = load16_nt(range_rsrc(x + t * (int64_t)H, 2 * H), 16 * u);
+    // experts and ranks of slots held .. held + 7; a small batch (inline scan)
+    // loads the first eight before its scan, to overlap the two round trips
+    // (in the prefill sizes, issuing them this early slowed the kernel)
+    int e8[8], rk8[8], held = -1;
+    if (t < T) {
+        a = load16_nt(range_rsrc(x + t * (int64_t)H, 2 * H), 16 * u);
+        if (MODE == kInline) {
+            load_slots(topk_idx, tile_rank, t * k, 0, k, e8, rk8);
+            held = 0;
+        }
+    }
     ScanView sv{expert_offsets, expert_counts, tile_base};
     __shared__ SmallLds Ls;
     if constexpr (MODE == kInline) {
@@ -684,10 +726,24 @@ __global__ __launch_bounds__(kScatterThreads) void k_scatter_bf16(
     const int64_t p0 = t * k;
     for (int j0 = 0; j0 < k; j0 += 8) {
         int r[8];
-        if constexpr (MODE == kRouted)
+        if constexpr (MODE == kRouted) {
             slot_rows_small(Ls, t, j0, k, max_rows, r);
-        else
-            slot_rows(topk_idx, tile_rank, sv.off, sv.tb + (t / TT) * E, p0, j0, k, E, max_rows, r);
+        } else {
+            const int32_t* tb = sv.tb + (t / TT) * E;
+            if constexpr (MODE == kInline) {
+                if constexpr (MODE == kInline) {
+                    if (j0 != held) {
+                        load_slots(topk_idx, tile_rank, p0, j0, k, e8, rk8);
+                        held = j0;
+                    }
+                    slot_rows(e8, rk8, sv.off, tb, E, max_rows, r);
+                } else {
+                    slot_rows(topk_idx, tile_rank, sv.off, tb, p0, j0, k, E, max_rows, r);
+                }
+            } else {
+                slot_rows(topk_idx, tile_rank, sv.off, tb, p0, j0, k, E, max_rows, r);
+            }
+        }
         if (chunk == 0) publish_rows(lane, p0, j0, k, r, dst_row, row_src);
         if (u < U) {
 #pragma unroll
@@ -733,6 +789,14 @@ __global__ __launch_bounds__(1024) void k_scatter_fp8(
         a0 = load16_nt(xr, 32 * (w * kWave + lane));
         b0 = load16_nt(xr, 32 * (w * kWave + lane) + 16);
     }
+    // experts and ranks of slots held .. held + 7; a small batch (inline scan)
+    // loads the first eight before its scan, to overlap the two round trips
+    // (in the prefill sizes, issuing them this early slowed the kernel)
+    int e8[8], rk8[8], held = -1;
+    if (MODE == kInline && !pad_block) {
+        load_slots(topk_idx, tile_rank, t * k, 0, k, e8, rk8);
+        held = 0;
+    }
     ScanView sv{expert_offsets, expert_counts, tile_base};
     __shared__ SmallLds Ls;
     if constexpr (MODE == kInline) {
@@ -776,10 +840,19 @@ __global__ __launch_bounds__(1024) void k_scatter_fp8(
         if (u < U && (u & 7) == 0) s_scale[u >> 3] = s;
         for (int j0 = 0; j0 < k; j0 += 8) {
             int r[8];
-            if constexpr (MODE == kRouted)
+            if constexpr (MODE == kRouted) {
                 slot_rows_small(Ls, t, j0, k, max_rows, r);
-            else
-                slot_rows(topk_idx, tile_rank, sv.off, tb, p0, j0, k, E, max_rows, r);
+            } else {
+                if constexpr (MODE == kInline) {
+                    if (j0 != held) {
+                        load_slots(topk_idx, tile_rank, p0, j0, k, e8, rk8);
+                        held = j0;
+                    }
+                    slot_rows(e8, rk8, sv.off, tb, E, max_rows, r);
+                } else {
+                    slot_rows(topk_idx, tile_rank, sv.off, tb, p0, j0, k, E, max_rows, r);
+                }
+            }
             if (chunk == 0) publish_rows(lane, p0, j0, k, r, dst_row, row_src);
             if (u < U) {
 #pragma unroll
