@@ -76,14 +76,17 @@ DispatchWorkspace dispatch_workspace(int64_t T, int E, int k) {
 // tile's counts counts[e] (the row padded with zeros to a multiple of 4
 // bytes) and rank[p] (the tile's slice of the [T, k] rank array; 0xFF for a
 // slot whose expert is outside [0, E), which the scatter never reads).
+// With zeroed, the caller has already cleared s_mask and synchronised.
 template <typename Ids>
 __device__ __forceinline__ void count_tile(Ids ids, int npairs, int k, int E, uint64_t* s_mask,
                                            uint8_t* __restrict__ counts,
-                                           uint8_t* __restrict__ rank) {
+                                           uint8_t* __restrict__ rank, bool zeroed = false) {
     const int NT = blockDim.x;
     const int tid = threadIdx.x;
-    for (int i = tid; i < E; i += NT) s_mask[i] = 0ull;
-    __syncthreads();
+    if (!zeroed) {
+        for (int i = tid; i < E; i += NT) s_mask[i] = 0ull;
+        __syncthreads();
+    }
     for (int p = tid; p < npairs; p += NT) {
         const int e = ids(p);
         if ((unsigned)e < (unsigned)E) atomicOr(&s_mask[e], 1ull << (p / k));
@@ -130,6 +133,8 @@ __global__ __launch_bounds__(1024) void k_route_count(const float* __restrict__ 
     const int64_t tile = blockIdx.x;
     const int64_t t0 = tile * a.TT;
     const int n = (int)min((int64_t)a.TT, a.T - t0);
+    // clear the masks while the logits are in flight
+    for (int i = threadIdx.x; i < a.E; i += blockDim.x) s_mask[i] = 0ull;
     if ((int)threadIdx.x < a.TT * S) {   // whole lane groups
         const int tl = threadIdx.x / S;
         const int g = threadIdx.x & (S - 1);
@@ -142,7 +147,7 @@ __global__ __launch_bounds__(1024) void k_route_count(const float* __restrict__ 
     }
     __syncthreads();
     count_tile([s_ids](int p) { return s_ids[p]; }, n * a.k, a.k, a.E, s_mask,
-               a.tile_counts + tile * ((a.E + 3) & ~3), a.tile_rank + t0 * a.k);
+               a.tile_counts + tile * ((a.E + 3) & ~3), a.tile_rank + t0 * a.k, true);
 }
 
 // ---------------------------------------------------------------- scan
