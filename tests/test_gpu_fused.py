@@ -37,11 +37,11 @@ def _host(b, R, fp8):
 
 
 def fused_case(T, H, E, k, groups=1, row_align=1, fp8=False, seed=0, zipf_s=None, dev=None,
-               bufs=None, logits_t=None, check_two_call=True):
+               bufs=None, logits_t=None, check_two_call=True, logits_np=None):
     from combine_moe_route_amd import alloc_dispatch, moe_dispatch, moe_route_dispatch, moe_route_topk
     log(f"[fused] T={T} H={H} E={E} k={k} G={groups} A={row_align} fp8={fp8} seed={seed}")
     x_np = gen_x_bf16(T, H, seed)
-    l_np = gen_logits(T, E, seed, zipf_s)
+    l_np = gen_logits(T, E, seed, zipf_s) if logits_np is None else logits_np
     x = to_dev_bf16(x_np, dev)
     logits = torch.from_numpy(l_np).to(dev) if logits_t is None else logits_t
     if bufs is None:
@@ -224,3 +224,24 @@ def test_fused_repeat_bit_identical(dev):
         else:
             for a, bb in zip(first, cur):
                 assert torch.equal(a, bb), f"run {it} differs"
+
+
+@pytest.mark.parametrize("i", range(40))
+def test_fused_fuzz(dev, i):
+    """Seeded random shapes across the three dispatch modes (one launch for
+    small batches with few experts, inline scan for small batches, scan
+    kernel) and the route-kernel fallbacks, with ties across the top-k
+    boundary in some cases; oracle-exact and bitwise equal to the two-call
+    path."""
+    rng = np.random.default_rng([4242, i])
+    E = int(rng.choice([4, 8, 12, 16, 44, 48, 52, 64, 65, 128, 256, 384, 768, 1000]))
+    k = int(rng.integers(1, min(E, 10) + 1))
+    G = int(rng.choice([g for g in (1, 2, 4, 8) if E % g == 0]))
+    A = int(rng.choice([1, 1, 8, 128]))
+    fp8 = bool(rng.random() < 0.5)
+    H = int(rng.choice([128, 256, 1024])) if fp8 else int(rng.choice([8, 64, 200, 1024]))
+    T = int(rng.choice([1, 7, 64, 128, 255, 256, 257, 1000, 1025, 4097]))
+    logits = gen_logits(T, E, i)
+    if rng.random() < 0.4:
+        logits = (np.round(logits * 2.0) / 2.0).astype(np.float32)
+    fused_case(T, H, E, k, G, A, fp8, seed=i, dev=dev, logits_np=logits)
