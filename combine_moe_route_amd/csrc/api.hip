@@ -204,9 +204,10 @@ int moe_route_dispatch(const float* logits, const void* x, int64_t T, int H, int
                        float* topk_w, void* out, float* out_scales, int32_t* expert_counts,
                        int32_t* expert_offsets, int32_t* group_offsets, int32_t* row_src,
                        int32_t* dst_row, void* workspace, size_t workspace_bytes, void* stream) {
-    // at least one of logits / topk_w must be non-null to select routing;
-    // a null one is then reported by the pointer checks
-    if (!logits && !topk_w) return T > 0 ? MOE_ENULL : MOE_OK;
+    // at least one of logits / topk_w must be non-null to select routing (a
+    // null one is then reported by the pointer checks); an empty batch needs
+    // neither and still writes zero counts and offsets
+    if (!logits && !topk_w && T > 0) return MOE_ENULL;
     return dispatch_impl(logits, topk_w, x, topk_idx, T, H, E, k, groups, row_align, out_dtype,
                          out, out_scales, expert_counts, expert_offsets, group_offsets, row_src,
                          dst_row, workspace, workspace_bytes, static_cast<hipStream_t>(stream));

@@ -165,6 +165,34 @@ def test_dispatch_validation():
     assert dispatch(wsb=lib.moe_dispatch_workspace_bytes(256, 8, 2, 1) - 4) == ENOSPC
 
 
+def test_route_dispatch_validation():
+    """moe_route_dispatch: the moe_dispatch checks plus the routing pointers;
+    every case here is rejected before any launch."""
+    def rd(**kw):
+        a = dict(logits=A + 2 ** 24, x=A, T=256, H=256, E=8, k=2, groups=1, row_align=1, dt=0,
+                 idx=B, w=B + 2 ** 19, out=A + 2 ** 20, scales=A + 2 ** 21, counts=B + 2 ** 20,
+                 offsets=B + 2 ** 20 + 64, goff=B + 2 ** 20 + 128, row_src=B + 2 ** 21,
+                 dst_row=B + 2 ** 22, ws=B + 2 ** 23, wsb=1 << 20)
+        a.update(kw)
+        return lib.moe_route_dispatch(a["logits"], a["x"], a["T"], a["H"], a["E"], a["k"],
+                                      a["groups"], a["row_align"], a["dt"], a["idx"], a["w"],
+                                      a["out"], a["scales"], a["counts"], a["offsets"], a["goff"],
+                                      a["row_src"], a["dst_row"], a["ws"], a["wsb"], None)
+    assert rd(k=0) == EINVAL
+    assert rd(k=9, E=8) == EINVAL
+    assert rd(groups=3) == EINVAL
+    assert rd(H=200, dt=1) == EINVAL
+    assert rd(logits=None, w=None) == ENULL
+    assert rd(logits=None) == ENULL
+    assert rd(w=None) == ENULL
+    assert rd(idx=None) == ENULL
+    assert rd(logits=A + 2 ** 24 + 2) == EALIGN
+    assert rd(w=B + 2 ** 19 + 1) == EALIGN
+    assert rd(wsb=16) == ENOSPC
+    assert rd(ws=None, wsb=1 << 20) == ENULL
+    assert rd(T=2 ** 29, k=8) == EINVAL                      # rows overflow int32
+
+
 def test_dispatch_no_alloc_validation():
     """The no-alloc variant checks everything before any HIP call; a request
     needing more scratch than the library's array holds is MOE_ENOSPC."""

@@ -138,6 +138,24 @@ def test_single_launch_ties(dev):
         assert np.array_equal(bf16_to_np(b.out[:ref.num_rows]), ref.out)
 
 
+def test_fused_empty_batch_writes_zero_offsets(dev):
+    """T = 0: no routing happens, and the counts and offsets are still
+    written (as zeros) over whatever the buffers held."""
+    from combine_moe_route_amd import alloc_dispatch, moe_route_dispatch
+    for E, k, G, A, fp8 in [(8, 2, 1, 1, False), (256, 8, 32, 128, True)]:
+        bufs = alloc_dispatch(0, 256, E, k, G, A, fp8, dev)
+        bufs.expert_counts.fill_(7)
+        bufs.expert_offsets.fill_(7)
+        bufs.group_offsets.fill_(7)
+        logits = torch.empty((0, E), dtype=torch.float32, device=dev)
+        x = torch.empty((0, 256), dtype=torch.bfloat16, device=dev)
+        moe_route_dispatch(logits, x, k, G, A, fp8, bufs)
+        torch.cuda.synchronize()
+        assert bufs.expert_counts.cpu().tolist() == [0] * E
+        assert bufs.expert_offsets.cpu().tolist() == [0] * (E + 1)
+        assert bufs.group_offsets.cpu().tolist() == [0] * (G + 1)
+
+
 def test_fused_unaligned_logits_fall_back(dev):
     """Logits not 16-byte aligned: the route kernel runs first."""
     T, E, k = 300, 256, 8
