@@ -280,6 +280,35 @@ def test_fp8_block_vs_torch_library_path():
         assert np.array_equal(q, want)
 
 
+def test_block_quantiser_batch_matches_single_and_torch():
+    """quantize_blocks, the reference of the whole-domain GPU sweep, on blocks
+    built like that sweep's (amax first, every other |x| <= amax, both signs,
+    amax from bf16 subnormals up to the largest finite bf16): per block the
+    same codes and scale as quantize_block, and the codes of torch's E4M3 cast
+    of the fp32 quotient x / (amax / 448), in the plain and the OpenMP build."""
+    rng = np.random.default_rng(9)
+    n = 3000
+    amax = np.concatenate([np.arange(1, 9), rng.integers(1, 0x7F80, n - 16),
+                           np.arange(0x7F78, 0x7F80)]).astype(np.uint16)
+    mags = np.floor(rng.random((n, 127)) * (amax[:, None].astype(np.float64) + 1)).astype(np.uint32)
+    mags = np.minimum(mags, amax[:, None].astype(np.uint32))
+    signs = rng.integers(0, 2, (n, 127)).astype(np.uint32) << 15
+    blocks = np.empty((n, 128), np.uint16)
+    blocks[:, 0] = amax
+    blocks[:, 1:] = (mags | signs).astype(np.uint16)
+    xt = torch.from_numpy(bf16_bits_to_f32(blocks).copy())
+    st = (xt[:, :1].abs() / 448.0)
+    want = (xt / st).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    for v in ("plain", "omp"):
+        with oracle.using(v):
+            q, s = oracle.quantize_blocks(blocks)
+        assert np.array_equal(s.view(np.uint32), st[:, 0].numpy().view(np.uint32)), v
+        assert np.array_equal(q, want), v
+    for i in range(0, n, 97):
+        qi, si = oracle.quantize_block(blocks[i])
+        assert np.array_equal(qi, q[i]) and np.float32(si).view(np.uint32) == s[i].view(np.uint32)
+
+
 def test_fp8_block_all_zero():
     q, s = oracle.quantize_block(np.zeros(128, np.uint16))
     assert s == 0.0 and np.all(q == 0)
