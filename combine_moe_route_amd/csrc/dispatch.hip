@@ -759,6 +759,18 @@ __global__ __launch_bounds__(kScatterThreads) void k_scatter_bf16(
     }
 }
 
+// Role of block b of a grid of T token blocks and P pad blocks: the pad
+// blocks are spread evenly among the token blocks (one every D = (T + P) / P
+// blocks), so that the pure writes of the pad rows mix with the reads and
+// writes of the token rows instead of coming all at once. Returns the token
+// index, or -1 - j for pad block j.
+__device__ __forceinline__ int64_t block_role(int64_t b, int64_t T, int64_t P) {
+    if (P == 0) return b;
+    const int64_t D = (T + P) / P;
+    if (b < P * D) return (b % D == D - 1) ? -1 - b / D : b - (b + 1) / D;
+    return b - P;
+}
+
 // FP8 rows. One block per token, W waves; wave w handles row chunks w, w+W,
 // ... of 64 lane units, a unit being 16 bf16 in (32 bytes) and 16 E4M3 codes
 // out (16 bytes), so each aligned group of 8 lanes holds one 1x128 block and
@@ -778,8 +790,9 @@ __global__ __launch_bounds__(1024) void k_scatter_fp8(
     float* __restrict__ scales, int32_t* __restrict__ row_src, int32_t* __restrict__ dst_row,
     RouteArgs ra) {
     extern __shared__ float s_scale[];             // [H / 128]
-    const bool pad_block = (int)blockIdx.x < pad_blocks;
-    const int64_t t = pad_block ? 0 : blockIdx.x - pad_blocks;
+    const int64_t role = block_role(blockIdx.x, T, pad_blocks);
+    const bool pad_block = role < 0;
+    const int64_t t = pad_block ? 0 : role;
     const int lane = threadIdx.x & (kWave - 1);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int W = blockDim.x / kWave;
@@ -816,7 +829,7 @@ __global__ __launch_bounds__(1024) void k_scatter_fp8(
         sv = ScanView{Ls.off, Ls.cnt, nullptr};
     }
     if (pad_block) {
-        zero_pad_rows(blockIdx.x, pad_blocks_per_expert, pad_rows_per_block, H, true, max_rows,
+        zero_pad_rows((int)(-1 - role), pad_blocks_per_expert, pad_rows_per_block, H, true, max_rows,
                       sv.cnt, sv.off, out, scales, row_src);
         return;
     }
