@@ -5,7 +5,7 @@
 namespace moe {
 
 namespace {
-constexpr int kCombineThreads = 256;
+constexpr int kCombineThreads = 128;
 constexpr int kCombineWaves = kCombineThreads / kWave;
 constexpr int kSlotBatch = 8;
 }  // namespace
