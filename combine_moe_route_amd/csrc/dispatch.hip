@@ -20,7 +20,7 @@
 //           tokens' bits). Both fit a byte: at most 64 tokens per tile. In
 //           moe_route_dispatch the same block first routes its tokens (top-k
 //           by sorting networks, topk_sort.h).
-//   scan    up to 32 blocks, each owning a range of tiles. Every block brings
+//   scan    up to 128 blocks, each owning a range of tiles. Every block brings
 //           all byte counts into LDS in batches of 16-byte loads (chunks of
 //           64 KiB), sums every expert's total and its prefix up to the
 //           block's first tile, and scans the totals, padded to row_align,
@@ -201,7 +201,8 @@ __device__ __forceinline__ int wave_inclusive_sum(int v) {
 // offsets in each block; block 0 writes them). Each block writes the tile
 // prefixes (relative to the segment start) of its own range only, so the
 // stores spread over the blocks and no block waits for another.
-constexpr int kScanBlocks = 32;
+// 128 blocks measured faster than 16, 32, 64 or 256 at both prefill shapes.
+constexpr int kScanBlocks = 128;
 constexpr int kScanShare = 4;   // at most this many threads per expert group
 
 __global__ __launch_bounds__(kScanThreads) void k_scan(const uint8_t* __restrict__ tile_counts,
