@@ -202,6 +202,9 @@ __device__ __forceinline__ int wave_inclusive_sum(int v) {
 // prefixes (relative to the segment start) of its own range only, so the
 // stores spread over the blocks and no block waits for another.
 // 128 blocks measured faster than 16, 32, 64 or 256 at both prefill shapes.
+// A block takes over half a CU's LDS, so one runs per CU: on a stream whose
+// CU mask leaves fewer CUs the grid shrinks to one block per CU, as a second
+// round of blocks would repeat the whole count read (3x the time on 32 CUs).
 constexpr int kScanBlocks = 128;
 constexpr int kScanShare = 4;   // at most this many threads per expert group
 
@@ -918,6 +921,19 @@ static void launch_route_count_k(int S, const DispatchArgs& a, const CountArgs& 
     }
 }
 
+// CUs the stream may run on (its CU mask; every CU for a stream without
+// one), or 0 if the runtime cannot say
+static int stream_cus(hipStream_t stream) {
+    uint32_t mask[32] = {};
+    if (hipExtStreamGetCUMask(stream, 32, mask) != hipSuccess) {
+        (void)hipGetLastError();   // a failed query is not the caller's error
+        return 0;
+    }
+    int n = 0;
+    for (uint32_t m : mask) n += __builtin_popcount(m);
+    return n;
+}
+
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream, LaunchInfo info[4], int* n,
                            bool run) {
     const DispatchWorkspace ws = dispatch_workspace(a.T, a.E, a.k);
@@ -931,9 +947,13 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream, LaunchInfo
     if (count_threads < kWave) count_threads = kWave;
     const size_t count_lds = (size_t)a.E * sizeof(uint64_t) +
                              (fused ? (size_t)TT * a.k * sizeof(int32_t) : 0);
-    const int64_t scan_blocks = tiles < 1 ? 1 : tiles < kScanBlocks ? tiles : kScanBlocks;
     // small batches scan inside the scatter (there must be scatter blocks)
     const bool inline_scan_ok = a.T > 0 && tiles <= kInlineTiles && tiles * a.E <= kInlineCells;
+    int64_t scan_blocks = tiles < 1 ? 1 : tiles < kScanBlocks ? tiles : kScanBlocks;
+    if (run && !inline_scan_ok && scan_blocks > 1) {
+        const int cus = stream_cus(stream);
+        if (cus > 0 && cus < scan_blocks) scan_blocks = cus;
+    }
     // small batches with few experts: every scatter block routes the whole
     // batch, so dispatch is one launch (the scatter's blocks have at least
     // kSmallTokens threads)
