@@ -23,14 +23,20 @@ def _snapshot(topk_idx, topk_w, bufs, y):
     return [t.clone() for t in out]
 
 
-@pytest.mark.parametrize("name", ["dsv3_decode", "mixtral_decode", "tiny"])
-def test_graph_replays_match_eager(name):
+@pytest.mark.parametrize("name,fused,H", [
+    ("dsv3_decode", False, None), ("mixtral_decode", False, None), ("tiny", False, None),
+    ("dsv3_decode", True, None), ("mixtral_decode", True, None),
+    # prefill batch sizes (narrower rows): the counting, scan and scatter launches
+    ("kimi_prefill", True, 1024), ("dsv3_prefill", True, 1024), ("dsv3_prefill", False, 1024),
+], ids=lambda v: str(v))
+def test_graph_replays_match_eager(name, fused, H):
+    """fused: moe_route_dispatch; else moe_route_topk then moe_dispatch."""
     from combine_moe_route_amd import (alloc_dispatch, moe_combine, moe_dispatch,
                                        moe_dispatch_max_rows, moe_harness_expert_scale,
-                                       moe_route_topk)
-    w = workload(name)
+                                       moe_route_dispatch, moe_route_topk)
+    w = workload(name) if H is None else workload(name, H=H)
     dev = torch.device("cuda:0")
-    log(f"graph capture {name}")
+    log(f"graph capture {name} fused={fused} H={w.H}")
     x = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev)
     logits = torch.empty((w.T, w.E), dtype=torch.float32, device=dev)
     topk_idx = torch.empty((w.T, w.k), dtype=torch.int32, device=dev)
@@ -46,8 +52,12 @@ def test_graph_replays_match_eager(name):
         logits.copy_(torch.from_numpy(l_np))
 
     def step():
-        moe_route_topk(logits, w.k, topk_idx, topk_w)
-        moe_dispatch(x, topk_idx, w.E, w.groups, w.row_align, w.fp8, bufs)
+        if fused:
+            moe_route_dispatch(logits, x, w.k, w.groups, w.row_align, w.fp8, bufs, topk_idx,
+                               topk_w)
+        else:
+            moe_route_topk(logits, w.k, topk_idx, topk_w)
+            moe_dispatch(x, topk_idx, w.E, w.groups, w.row_align, w.fp8, bufs)
         moe_harness_expert_scale(bufs, topk_idx, w.E, w.fp8, expert_out=expert_out)
         moe_combine(expert_out, bufs.dst_row, topk_w, y)
 
