@@ -161,7 +161,9 @@ size_t moe_dispatch_workspace_bytes(int64_t T, int E, int k, int groups);
  * moe_dispatch_max_rows(T, E, k, row_align). T == 0 writes zero counts and
  * offsets. Three kernels: per-tile counts and ranks, the scan into offsets,
  * the rows (two for batches of at most 64 count tiles, whose row kernel
- * does the scan).
+ * does the scan). On a stream created with a CU mask the scan kernel runs
+ * one block per CU of the mask (at most 128); the results do not depend on
+ * the mask.
  */
 int moe_dispatch(const void* x, const int32_t* topk_idx,
                  int64_t T, int H, int E, int k, int groups, int row_align,
