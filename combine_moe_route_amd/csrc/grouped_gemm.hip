@@ -11,7 +11,8 @@
 // 128-element interval of the inner dimension, and that partial is scaled by
 // both block scales and added into fp32 accumulators held in vector
 // registers. On gfx950 one v_mfma_f32_16x16x128_f8f6f4 covers exactly one
-// interval for a 16x16 output tile, so each MFMA result is promoted at once.
+// interval for a 16x16 output tile, so each MFMA result is promoted right
+// away (the last row group of a k-block at the start of the next one).
 //
 // Work split: segments are cut into row tiles (a small kernel lists them
 // from the device-side offsets, so the host never reads them); a workgroup
@@ -235,6 +236,13 @@ __device__ __forceinline__ void gemm_body(
         for (int j = 0; j < 4 * SH::kHalves; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int half = lane >> 4;
+    // The last row group's MFMA results of a k-block, promoted at the start of
+    // the next one (zeros before the first: adding +0 products to the +0 start
+    // of the accumulators changes nothing).
+    f32x4 pend[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) pend[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float pend_f = 0.0f;
     // One k-block from stage st; the DMA into stage nst (k-block nb) is
     // issued first.
     auto compute = [&](auto st, auto nst, int nb) {
@@ -250,6 +258,14 @@ __device__ __forceinline__ void gemm_body(
         i32x8 xf[4];
 #pragma unroll
         for (int i = 0; i < 4; i++) xf[i] = frag(A, wm * 64 + i * 16 + (lane & 15), half);
+        // the previous k-block's last promotion, while the fragments load
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int r = 0; r < 4; r++)
+                acc[3][(SH::kHalves - 1) * 4 + j][r] =
+                    fmaf(pend[j][r], pend_f, acc[3][(SH::kHalves - 1) * 4 + j][r]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int hh = 0; hh < SH::kHalves; hh++) {
             i32x8 wf[4];
@@ -282,11 +298,18 @@ __device__ __forceinline__ void gemm_body(
                 for (int j = 0; j < 4; j++) prev[j] = cur[j];
                 __builtin_amdgcn_sched_barrier(0);
             }
+            if (hh + 1 < SH::kHalves) {
 #pragma unroll
-            for (int j = 0; j < 4; j++)
+                for (int j = 0; j < 4; j++)
 #pragma unroll
-                for (int r = 0; r < 4; r++)
-                    acc[3][hh * 4 + j][r] = fmaf(prev[j][r], f[3], acc[3][hh * 4 + j][r]);
+                    for (int r = 0; r < 4; r++)
+                        acc[3][hh * 4 + j][r] = fmaf(prev[j][r], f[3], acc[3][hh * 4 + j][r]);
+            } else {
+                // promoted at the start of the next k-block (or after the loop)
+#pragma unroll
+                for (int j = 0; j < 4; j++) pend[j] = prev[j];
+                pend_f = f[3];
+            }
         }
     };
 
@@ -318,6 +341,12 @@ __device__ __forceinline__ void gemm_body(
         if (b + 1 < KB) step(std::integral_constant<int, 1>{}, b + 1);
     // No LDS DMA may still be writing when the workgroup's LDS is released.
     wait_vmcnt<0>();
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+        for (int r = 0; r < 4; r++)
+            acc[3][(SH::kHalves - 1) * 4 + j][r] =
+                fmaf(pend[j][r], pend_f, acc[3][(SH::kHalves - 1) * 4 + j][r]);
 
     // Lane holds, for fragment pair (i, j), row 16i + lane%16 and the four
     // consecutive columns 16j + 4*(lane/16) .. +3.
