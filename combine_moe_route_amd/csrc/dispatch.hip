@@ -274,10 +274,12 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(const uint8_t* __restrict
         const int r0 = min(nt, p * per);
         const int r1 = min(nt, r0 + per);
         if (real) {
-            column_sum4(s_cnt, r0, r1, Q, q, all);
-            const int64_t before_mine = my0 - c0;   // rows of this chunk before my0
-            if (before_mine > r0)
-                column_sum4(s_cnt, r0, (int)min((int64_t)r1, before_mine), Q, q, pre);
+            // rows of this chunk before my0 count into the prefix as well:
+            // [r0, r1) splits at that point, each row is read once
+            const int64_t before_mine = my0 - c0;
+            const int rm = (int)max((int64_t)r0, min((int64_t)r1, before_mine));
+            column_sum4(s_cnt, r0, rm, Q, q, pre);
+            column_sum4(s_cnt, rm, r1, Q, q, all);
         }
         last_c0 = c0;
         last_nt = nt;
@@ -285,7 +287,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(const uint8_t* __restrict
     const bool staged_mine = last_c0 <= my0 && my1 <= last_c0 + last_nt;
 #pragma unroll
     for (int b = 0; b < 4; b++) {
-        s_all[b][tid] = all[b];
+        s_all[b][tid] = all[b] + pre[b];
         s_pre[b][tid] = pre[b];
     }
     __syncthreads();
